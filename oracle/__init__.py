@@ -1,0 +1,187 @@
+"""CPU oracle for the FP32 row-reduction family — test infrastructure only.
+
+Wraps ``oracle.c`` (plain fp64 C loops, one rounding to float32 per output)
+with numpy-in / numpy-out functions. Only ``tests/``, the package smoke check
+and the benchmark's CPU-baseline leg may import this package; the product
+path never does, and this package imports nothing from the product.
+
+Each function states the definition it computes; ``oracle.c`` cites the page
+passage each one follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i64 = ctypes.c_int64
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared",
+                               "-ffp-contract=off", "-fno-fast-math",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_rmsnorm_f32.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, ctypes.c_float]
+        lib.oracle_row_sum_f32.argtypes = [_f32p, _f32p, _i64, _i64]
+        lib.oracle_softmax_f32.argtypes = [_f32p, _f32p, _i64, _i64]
+        lib.oracle_layernorm_f32.argtypes = [_f32p, _f32p, _f32p, _f32p, _i64, _i64,
+                                             ctypes.c_float, _f64p]
+        lib.oracle_residual_layernorm_f32.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
+                                                      _i64, _i64, ctypes.c_float, _f64p]
+        lib.oracle_cross_entropy_f32.argtypes = [_f32p, _i32p, _f32p, _i64, _i64]
+        lib.oracle_owner.argtypes = [_i64, _i64, _i64, _i64p, _i64p]
+        lib.oracle_owner.restype = None
+        lib.oracle_logical_index.argtypes = [_i64, _i64, _i64, _i64]
+        lib.oracle_logical_index.restype = _i64
+        lib.oracle_slot_bound.argtypes = [_i64, _i64, _i64]
+        lib.oracle_slot_bound.restype = _i64
+        _lib = lib
+    return _lib
+
+
+def _f32(a, ndim):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if a.ndim != ndim:
+        raise ValueError(f"expected {ndim}-d array, got shape {a.shape}")
+    return a
+
+
+def _p(a, t):
+    return a.ctypes.data_as(t)
+
+
+def _check(rc):
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (rows < 0 or cols <= 0)")
+
+
+def rmsnorm(x, w, eps):
+    """y[r,c] = x[r,c]*w[c] / sqrt(mean_c x[r,c]^2 + eps)."""
+    x = _f32(x, 2)
+    w = _f32(w, 1)
+    rows, cols = x.shape
+    assert w.shape == (cols,)
+    y = np.empty_like(x)
+    _check(_load().oracle_rmsnorm_f32(_p(x, _f32p), _p(w, _f32p), _p(y, _f32p), rows, cols, eps))
+    return y
+
+
+def row_sum(x):
+    """out[r] = sum_c x[r,c]."""
+    x = _f32(x, 2)
+    rows, cols = x.shape
+    out = np.empty(rows, np.float32)
+    _check(_load().oracle_row_sum_f32(_p(x, _f32p), _p(out, _f32p), rows, cols))
+    return out
+
+
+def softmax(x):
+    """y[r,c] = exp(x[r,c]-m_r) / sum_k exp(x[r,k]-m_r), m_r the row maximum."""
+    x = _f32(x, 2)
+    rows, cols = x.shape
+    y = np.empty_like(x)
+    _check(_load().oracle_softmax_f32(_p(x, _f32p), _p(y, _f32p), rows, cols))
+    return y
+
+
+def layernorm(x, gamma, beta, eps):
+    """y = (x-mean)/sqrt(var+eps)*gamma + beta, population variance per row."""
+    x = _f32(x, 2)
+    g = _f32(gamma, 1)
+    b = _f32(beta, 1)
+    rows, cols = x.shape
+    y = np.empty_like(x)
+    scratch = np.empty(cols, np.float64)
+    _check(_load().oracle_layernorm_f32(_p(x, _f32p), _p(g, _f32p), _p(b, _f32p), _p(y, _f32p),
+                                        rows, cols, eps, _p(scratch, _f64p)))
+    return y
+
+
+def residual_layernorm(x, residual, gamma, beta, eps):
+    """h = fl32(x + residual); y = LayerNorm(h). Returns (y, h)."""
+    x = _f32(x, 2)
+    r = _f32(residual, 2)
+    g = _f32(gamma, 1)
+    b = _f32(beta, 1)
+    rows, cols = x.shape
+    assert r.shape == x.shape
+    y = np.empty_like(x)
+    h = np.empty_like(x)
+    scratch = np.empty(cols, np.float64)
+    _check(_load().oracle_residual_layernorm_f32(_p(x, _f32p), _p(r, _f32p), _p(g, _f32p),
+                                                 _p(b, _f32p), _p(y, _f32p), _p(h, _f32p),
+                                                 rows, cols, eps, _p(scratch, _f64p)))
+    return y, h
+
+
+def cross_entropy(logits, targets):
+    """loss[r] = logsumexp_c x[r,c] - x[r,t[r]]; NaN for a target outside [0, cols)."""
+    x = _f32(logits, 2)
+    t = np.ascontiguousarray(targets, dtype=np.int32)
+    rows, cols = x.shape
+    assert t.shape == (rows,)
+    loss = np.empty(rows, np.float32)
+    _check(_load().oracle_cross_entropy_f32(_p(x, _f32p), _p(t, _i32p), _p(loss, _f32p), rows, cols))
+    return loss
+
+
+def owner(i, W, V):
+    """(worker, slot) of logical element i under W workers with V consecutive elements each."""
+    wk = ctypes.c_int64()
+    sl = ctypes.c_int64()
+    _load().oracle_owner(i, W, V, ctypes.byref(wk), ctypes.byref(sl))
+    return wk.value, sl.value
+
+
+def logical_index(worker, slot, W, V):
+    """Logical element held in private `slot` of `worker`."""
+    return _load().oracle_logical_index(worker, slot, W, V)
+
+
+def slot_bound(N, W, V):
+    """Largest count of valid private slots of any worker for a row of N elements."""
+    return _load().oracle_slot_bound(N, W, V)
+
+
+def run(op: str, wl_arrays: dict):
+    """Dispatch by operator name; `wl_arrays` holds x, w, beta, residual, targets, eps."""
+    a = wl_arrays
+    if op == "rmsnorm":
+        return rmsnorm(a["x"], a["w"], a["eps"])
+    if op == "sum":
+        return row_sum(a["x"])
+    if op == "softmax":
+        return softmax(a["x"])
+    if op == "layernorm":
+        return layernorm(a["x"], a["w"], a["beta"], a["eps"])
+    if op == "residual_layernorm":
+        return residual_layernorm(a["x"], a["residual"], a["w"], a["beta"], a["eps"])
+    if op == "cross_entropy":
+        return cross_entropy(a["x"], a["targets"])
+    raise ValueError(op)

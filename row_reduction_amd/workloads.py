@@ -1,0 +1,156 @@
+"""Seeded synthetic inputs for the FP32 row-reduction family.
+
+This module only draws random numbers; it holds none of the reductions'
+arithmetic. Both the HIP path (through its tests and the benchmark) and the
+CPU oracle consume what it returns, so they always see identical inputs.
+
+Workloads follow the shapes the LuisaCompute "Consecutive-worker reduction
+layout checkpoint" page measures (RMSNorm table in its "Result" section:
+1x127, 17x257, 64x4096, 1024x4096) plus a bandwidth-bound 16384x8192 RMSNorm
+and the five sibling operators named in its "Evidence and what remains"
+section (sum, softmax, LayerNorm, residual LayerNorm, cross-entropy).
+
+Distribution notation: N(mu, sigma) takes sigma as the standard deviation;
+U(a, b) is uniform on [a, b). Values are drawn in float64 and rounded once
+to float32, except the 16384x8192 input, which is drawn in float32 directly
+(standard normal) to bound host memory and time.
+
+Seeds: workload family k (1..5) uses numpy's PCG64 ``default_rng(1000 + k)``;
+held-out replays of the plan selector use ``2000 + k``. Draw order within one
+shape: x, outlier positions, weight / gamma, beta, residual, targets.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+RMSNORM_EPS = 1e-6
+LAYERNORM_EPS = 1e-5
+
+# (rows, cols) of the measured shapes.
+SHAPE_1x127 = (1, 127)
+SHAPE_17x257 = (17, 257)
+SHAPE_64x4096 = (64, 4096)
+SHAPE_1024x4096 = (1024, 4096)
+SHAPE_16384x8192 = (16384, 8192)
+FAMILY_SHAPES = (SHAPE_1x127, SHAPE_17x257, SHAPE_64x4096, SHAPE_1024x4096)
+
+OPS = ("rmsnorm", "sum", "softmax", "layernorm", "residual_layernorm", "cross_entropy")
+
+
+@dataclass
+class Workload:
+    """One seeded input set. Arrays are C-contiguous; floats are float32."""
+
+    name: str
+    op: str
+    rows: int
+    cols: int
+    x: np.ndarray
+    eps: float = 0.0
+    w: np.ndarray | None = None          # RMSNorm weight or LayerNorm gamma
+    beta: np.ndarray | None = None       # LayerNorm beta
+    residual: np.ndarray | None = None   # residual LayerNorm second input
+    targets: np.ndarray | None = None    # cross-entropy class indices (int32)
+    meta: dict = field(default_factory=dict)
+
+
+def _normal_f32(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
+    if int(np.prod(shape)) >= (1 << 26):
+        a = rng.standard_normal(shape, dtype=np.float32)
+        if sigma != 1.0:
+            a *= np.float32(sigma)
+        return a
+    return np.ascontiguousarray(rng.normal(0.0, sigma, size=shape).astype(np.float32))
+
+
+def _uniform_f32(rng: np.random.Generator, n: int, lo: float, hi: float) -> np.ndarray:
+    return np.ascontiguousarray(rng.uniform(lo, hi, size=n).astype(np.float32))
+
+
+def rmsnorm_workload(rows: int, cols: int, seed: int, outlier_fraction: float = 0.0,
+                     name: str | None = None) -> Workload:
+    """x ~ N(0,1) (optionally with a fraction of entries scaled by 100), w ~ U(0.5,1.5)."""
+    rng = np.random.default_rng(seed)
+    x = _normal_f32(rng, (rows, cols), 1.0)
+    n_out = 0
+    if outlier_fraction > 0.0:
+        n_out = int(round(outlier_fraction * rows * cols))
+        idx = rng.choice(rows * cols, size=n_out, replace=False)
+        flat = x.reshape(-1)
+        flat[idx] *= np.float32(100.0)
+    w = _uniform_f32(rng, cols, 0.5, 1.5)
+    return Workload(name or f"rmsnorm_{rows}x{cols}", "rmsnorm", rows, cols, x,
+                    eps=RMSNORM_EPS, w=w, meta={"seed": seed, "outliers": n_out})
+
+
+def family_inputs(rows: int, cols: int, seed: int) -> dict[str, np.ndarray]:
+    """x ~ N(0,2), gamma ~ U(0.5,1.5), beta ~ N(0,0.1), residual ~ N(0,1), targets ~ U[0,cols)."""
+    rng = np.random.default_rng(seed)
+    x = _normal_f32(rng, (rows, cols), 2.0)
+    gamma = _uniform_f32(rng, cols, 0.5, 1.5)
+    beta = _normal_f32(rng, (cols,), 0.1)
+    residual = _normal_f32(rng, (rows, cols), 1.0)
+    targets = np.ascontiguousarray(rng.integers(0, cols, size=rows, dtype=np.int32))
+    return {"x": x, "gamma": gamma, "beta": beta, "residual": residual, "targets": targets}
+
+
+def family_workload(op: str, rows: int, cols: int, seed: int) -> Workload:
+    """One operator of the reduction family on the shared N(0,2) input set."""
+    if op not in OPS:
+        raise ValueError(f"unknown op {op!r}")
+    d = family_inputs(rows, cols, seed)
+    wl = Workload(f"{op}_{rows}x{cols}", op, rows, cols, d["x"], meta={"seed": seed})
+    if op == "rmsnorm":
+        wl.w, wl.eps = d["gamma"], RMSNORM_EPS
+    elif op in ("layernorm", "residual_layernorm"):
+        wl.w, wl.beta, wl.eps = d["gamma"], d["beta"], LAYERNORM_EPS
+        if op == "residual_layernorm":
+            wl.residual = d["residual"]
+    elif op == "cross_entropy":
+        wl.targets = d["targets"]
+    return wl
+
+
+def config_workloads(k: int, held_out: bool = False, include_large: bool = True) -> list[Workload]:
+    """The seeded workloads of measured configuration k (1..5).
+
+    1: RMSNorm 1x127; 2: RMSNorm 17x257; 3: RMSNorm 64x4096 with 1% outliers x100;
+    4: RMSNorm 1024x4096 and 16384x8192; 5: the five sibling operators on the
+    four page shapes with x ~ N(0,2).
+    """
+    seed = (2000 if held_out else 1000) + k
+    if k == 1:
+        return [rmsnorm_workload(*SHAPE_1x127, seed)]
+    if k == 2:
+        return [rmsnorm_workload(*SHAPE_17x257, seed)]
+    if k == 3:
+        return [rmsnorm_workload(*SHAPE_64x4096, seed, outlier_fraction=0.01)]
+    if k == 4:
+        out = [rmsnorm_workload(*SHAPE_1024x4096, seed)]
+        if include_large:
+            out.append(rmsnorm_workload(*SHAPE_16384x8192, seed))
+        return out
+    if k == 5:
+        return [family_workload(op, r, c, seed) for (r, c) in FAMILY_SHAPES
+                for op in OPS if op != "rmsnorm"]
+    raise ValueError(f"no configuration {k}")
+
+
+def algorithmic_bytes(op: str, rows: int, cols: int, with_h_out: bool = False) -> int:
+    """Bytes one call must move at minimum: each input read once, each output written once."""
+    rc = rows * cols
+    if op == "rmsnorm":
+        return 8 * rc + 4 * cols
+    if op == "sum":
+        return 4 * rc + 4 * rows
+    if op == "softmax":
+        return 8 * rc
+    if op == "layernorm":
+        return 8 * rc + 8 * cols
+    if op == "residual_layernorm":
+        return 12 * rc + 8 * cols + (4 * rc if with_h_out else 0)
+    if op == "cross_entropy":
+        return 4 * rc + 8 * rows
+    raise ValueError(op)

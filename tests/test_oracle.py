@@ -1,0 +1,295 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test checks the oracle against something other than itself: a library
+routine computing the same textbook definition in float64 (torch CPU, scipy,
+math.fsum), a closed form, an invariant of the mathematics, or the worked
+ownership example printed in the LuisaCompute "Consecutive-worker reduction
+layout checkpoint" page ("Implementation and semantics" section).
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import oracle
+from row_reduction_amd import workloads
+
+TINY_COLS = (1, 2, 3, 31, 33, 127, 128, 129, 257)
+
+
+def ulp_close(a, b, n_ulp=1):
+    """|a - b| <= n_ulp units in the last place of float32 b, elementwise."""
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    spacing = np.spacing(np.abs(b)).astype(np.float64)
+    return np.all(np.abs(a.astype(np.float64) - b.astype(np.float64)) <= n_ulp * spacing)
+
+
+def family(rows, cols, seed=7):
+    return workloads.family_inputs(rows, cols, seed)
+
+
+def t64(a):
+    return torch.from_numpy(np.asarray(a, np.float64))
+
+
+# ---------------------------------------------------------------- library routines
+
+@pytest.mark.parametrize("cols", TINY_COLS)
+@pytest.mark.parametrize("rows", [1, 5])
+def test_rmsnorm_matches_torch_rms_norm_f64(rows, cols):
+    wl = workloads.rmsnorm_workload(rows, cols, seed=11 + cols)
+    y = oracle.rmsnorm(wl.x, wl.w, wl.eps)
+    ref = F.rms_norm(t64(wl.x), (cols,), weight=t64(wl.w), eps=float(np.float32(wl.eps)))
+    assert ulp_close(y, ref.numpy().astype(np.float32))
+
+
+def test_rmsnorm_outlier_shape_matches_torch():
+    wl = workloads.config_workloads(3)[0]
+    y = oracle.rmsnorm(wl.x, wl.w, wl.eps)
+    ref = F.rms_norm(t64(wl.x), (wl.cols,), weight=t64(wl.w), eps=float(np.float32(wl.eps)))
+    assert wl.meta["outliers"] == round(0.01 * 64 * 4096)
+    assert ulp_close(y, ref.numpy().astype(np.float32))
+
+
+@pytest.mark.parametrize("cols", TINY_COLS)
+def test_softmax_matches_scipy(cols):
+    x = family(5, cols)["x"]
+    y = oracle.softmax(x)
+    ref = scipy.special.softmax(x.astype(np.float64), axis=1).astype(np.float32)
+    assert ulp_close(y, ref)
+
+
+@pytest.mark.parametrize("cols", TINY_COLS)
+def test_layernorm_matches_torch_layer_norm_f64(cols):
+    d = family(5, cols)
+    eps = workloads.LAYERNORM_EPS
+    y = oracle.layernorm(d["x"], d["gamma"], d["beta"], eps)
+    ref = F.layer_norm(t64(d["x"]), (cols,), t64(d["gamma"]), t64(d["beta"]),
+                       eps=float(np.float32(eps)))
+    # y = z*gamma + beta can cancel; compare against the f64 result's own scale.
+    ref = ref.numpy()
+    err = np.abs(y.astype(np.float64) - ref)
+    assert np.all(err <= np.spacing(np.abs(ref).astype(np.float32)) + 1e-12)
+
+
+@pytest.mark.parametrize("cols", TINY_COLS)
+def test_residual_layernorm_h_is_float32_sum_and_y_matches_torch(cols):
+    d = family(5, cols)
+    eps = workloads.LAYERNORM_EPS
+    y, h = oracle.residual_layernorm(d["x"], d["residual"], d["gamma"], d["beta"], eps)
+    h_ref = d["x"] + d["residual"]                    # numpy float32 add: one rounding
+    assert np.array_equal(h.view(np.int32), h_ref.view(np.int32))
+    ref = F.layer_norm(t64(h_ref), (cols,), t64(d["gamma"]), t64(d["beta"]),
+                       eps=float(np.float32(eps))).numpy()
+    err = np.abs(y.astype(np.float64) - ref)
+    assert np.all(err <= np.spacing(np.abs(ref).astype(np.float32)) + 1e-12)
+
+
+@pytest.mark.parametrize("cols", TINY_COLS)
+def test_cross_entropy_matches_torch_f64(cols):
+    d = family(5, cols)
+    loss = oracle.cross_entropy(d["x"], d["targets"])
+    ref = F.cross_entropy(t64(d["x"]), torch.from_numpy(d["targets"].astype(np.int64)),
+                          reduction="none").numpy()
+    err = np.abs(loss.astype(np.float64) - ref)
+    assert np.all(err <= np.spacing(np.abs(ref).astype(np.float32)) + 1e-12)
+
+
+@pytest.mark.parametrize("cols", TINY_COLS)
+def test_row_sum_matches_fsum(cols):
+    x = family(5, cols)["x"]
+    out = oracle.row_sum(x)
+    ref = np.array([math.fsum(map(float, row)) for row in x], np.float64)
+    err = np.abs(out.astype(np.float64) - ref)
+    assert np.all(err <= np.spacing(np.abs(ref).astype(np.float32)) + 1e-30)
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("c", [0.75, -0.75, 3.0, 1e-3, -2.5])
+@pytest.mark.parametrize("cols", [1, 33, 257])
+def test_rmsnorm_constant_row_closed_form(c, cols):
+    """Constant row c: y = sign(c) * w * |c| / sqrt(c^2 + eps)."""
+    eps = np.float32(1e-6)
+    x = np.full((2, cols), c, np.float32)
+    w = np.linspace(0.5, 1.5, cols, dtype=np.float32)
+    y = oracle.rmsnorm(x, w, eps)
+    cf = float(np.float32(c))
+    ref = np.array([math.copysign(1.0, cf) * float(wc) * abs(cf) / math.sqrt(cf * cf + float(eps))
+                    for wc in w], np.float64).astype(np.float32)
+    assert ulp_close(y, np.broadcast_to(ref, y.shape))
+
+
+@pytest.mark.parametrize("cols", [1, 2, 31, 128, 257, 4103])
+def test_softmax_constant_row_is_uniform(cols):
+    y = oracle.softmax(np.full((3, cols), -1.25, np.float32))
+    assert np.all(y == np.float32(1.0 / cols))
+
+
+@pytest.mark.parametrize("cols", [1, 2, 31, 128, 257, 4103])
+def test_cross_entropy_constant_row_is_log_cols(cols):
+    x = np.full((3, cols), 0.5, np.float32)
+    loss = oracle.cross_entropy(x, np.array([0, cols - 1, cols // 2], np.int32))
+    assert ulp_close(loss, np.full(3, math.log(cols), np.float32))
+
+
+@pytest.mark.parametrize("cols", [1, 2, 31, 128, 257])
+def test_layernorm_constant_row_gives_beta(cols):
+    d = family(2, cols)
+    x = np.full((2, cols), 0.75, np.float32)
+    y = oracle.layernorm(x, d["gamma"], d["beta"], 1e-5)
+    assert np.array_equal(y, np.broadcast_to(d["beta"], y.shape))
+
+
+@pytest.mark.parametrize("cols", [1, 31, 257, 4096])
+def test_row_sum_small_integers_exact(cols):
+    x = np.full((2, cols), 3.0, np.float32)
+    x[1] = np.arange(cols) % 7 - 3
+    out = oracle.row_sum(x)
+    assert out[0] == 3.0 * cols and out[1] == float(np.sum(np.arange(cols) % 7 - 3))
+
+
+def test_cols_one_special_cases():
+    x = np.array([[2.0], [-0.5], [0.0]], np.float32)
+    assert np.all(oracle.softmax(x) == 1.0)
+    assert np.all(oracle.cross_entropy(x, np.zeros(3, np.int32)) == 0.0)
+    assert np.array_equal(oracle.layernorm(x, [2.0], [0.25], 1e-5), np.full((3, 1), 0.25, np.float32))
+    assert np.array_equal(oracle.row_sum(x), x[:, 0])
+
+
+# ---------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("k", [-3, 1, 5])
+def test_rmsnorm_power_of_two_scale_invariance_bitwise(k):
+    wl = workloads.rmsnorm_workload(5, 257, seed=3)
+    y1 = oracle.rmsnorm(wl.x, wl.w, 0.0)
+    y2 = oracle.rmsnorm(wl.x * np.float32(2.0 ** k), wl.w, 0.0)
+    assert np.array_equal(y1.view(np.int32), y2.view(np.int32))
+
+
+@pytest.mark.parametrize("alpha", [0.3, 7.0, 1234.5])
+def test_rmsnorm_positive_scale_invariance(alpha):
+    wl = workloads.rmsnorm_workload(5, 129, seed=4)
+    y1 = oracle.rmsnorm(wl.x, wl.w, 0.0)
+    y2 = oracle.rmsnorm((wl.x.astype(np.float64) * alpha).astype(np.float32), wl.w, 0.0)
+    assert np.all(np.abs(y1 - y2) <= 1e-5 + 1e-5 * np.abs(y1))
+
+
+def test_rmsnorm_unit_magnitude_identity():
+    """x in {-1, +1}, w = 1, eps = 0 gives y = x exactly (mean square is 1)."""
+    rng = np.random.default_rng(0)
+    x = np.where(rng.random((4, 257)) < 0.5, -1.0, 1.0).astype(np.float32)
+    y = oracle.rmsnorm(x, np.ones(257, np.float32), 0.0)
+    assert np.array_equal(y, x)
+
+
+def test_rmsnorm_signed_zero():
+    x = np.array([[-0.0, 1.0, 0.0, -2.0]], np.float32)
+    y = oracle.rmsnorm(x, np.ones(4, np.float32), 1e-6)
+    assert np.signbit(y[0, 0]) and not np.signbit(y[0, 2])
+
+
+@pytest.mark.parametrize("cols", [1, 31, 127, 257, 4103])
+def test_softmax_rows_sum_to_one(cols):
+    y = oracle.softmax(family(5, cols)["x"])
+    assert np.all(y >= 0) and np.all(y <= 1)
+    assert np.all(np.abs(y.astype(np.float64).sum(axis=1) - 1.0) <= 1e-5)
+
+
+def test_softmax_shift_invariance_bitwise():
+    rng = np.random.default_rng(1)
+    x = (rng.integers(-512, 512, size=(4, 129)) / 64.0).astype(np.float32)  # exact in f32
+    assert np.array_equal(oracle.softmax(x), oracle.softmax(x + np.float32(4.0)))
+
+
+def test_cross_entropy_is_negative_log_softmax_at_target():
+    d = family(5, 257)
+    loss = oracle.cross_entropy(d["x"], d["targets"])
+    p = oracle.softmax(d["x"])[np.arange(5), d["targets"]].astype(np.float64)
+    assert np.all(loss >= 0)
+    assert np.all(np.abs(loss + np.log(p)) <= 1e-5 + 1e-5 * np.abs(loss))
+
+
+def test_cross_entropy_target_out_of_range_is_nan():
+    x = family(3, 33)["x"]
+    loss = oracle.cross_entropy(x, np.array([-1, 33, 0], np.int32))
+    assert np.isnan(loss[0]) and np.isnan(loss[1]) and np.isfinite(loss[2])
+
+
+def test_residual_layernorm_zero_residual_equals_layernorm():
+    d = family(5, 257)
+    y, h = oracle.residual_layernorm(d["x"], np.zeros_like(d["x"]), d["gamma"], d["beta"], 1e-5)
+    assert np.array_equal(h, d["x"])
+    assert np.array_equal(y, oracle.layernorm(d["x"], d["gamma"], d["beta"], 1e-5))
+
+
+def test_layernorm_unit_affine_moments():
+    d = family(5, 4096)
+    x = d["x"].astype(np.float64)
+    eps = 1e-5
+    y = oracle.layernorm(d["x"], np.ones(4096, np.float32), np.zeros(4096, np.float32), eps)
+    var = x.var(axis=1)
+    yd = y.astype(np.float64)
+    assert np.all(np.abs(yd.mean(axis=1)) <= 1e-6)
+    assert np.allclose((yd ** 2).mean(axis=1), var / (var + np.float32(eps)), rtol=1e-6, atol=0)
+
+
+def test_rejects_bad_shape():
+    with pytest.raises(ValueError):
+        oracle.rmsnorm(np.zeros((2, 0), np.float32), np.zeros(0, np.float32), 1e-6)
+
+
+# ---------------------------------------------------------------- ownership map
+
+def _golden_rows(name):
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", name)
+    rows = []
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([int(v) for v in line.split()])
+    return rows
+
+
+def test_ownership_matches_printed_w4_v2_example():
+    W, V = 4, 2
+    rows = _golden_rows("ownership_w4_v2.txt")
+    assert len(rows) == 8
+    for chunk, worker, e0, e1 in rows:
+        for element, i in enumerate((e0, e1)):
+            slot = chunk * V + element
+            assert oracle.logical_index(worker, slot, W, V) == i
+            assert oracle.owner(i, W, V) == (worker, slot)
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 8, 32, 64, 96, 256])
+@pytest.mark.parametrize("V", [1, 2, 4, 8])
+def test_ownership_bijection_and_slot_bound_brute_force(W, V):
+    for N in list(range(0, 70)) + [127, 128, 129, 257, 1000, 4103]:
+        seen = set()
+        per_worker = {}
+        for i in range(N):
+            wk, sl = oracle.owner(i, W, V)
+            assert 0 <= wk < W
+            assert (wk, sl) not in seen
+            seen.add((wk, sl))
+            assert oracle.logical_index(wk, sl, W, V) == i
+            per_worker[wk] = per_worker.get(wk, 0) + 1
+        brute = max(per_worker.values()) if per_worker else 0
+        assert oracle.slot_bound(N, W, V) == brute, (N, W, V)
+
+
+def test_page_plans_slot_counts_by_enumeration():
+    """The page's chosen worker/V pairs: the bound equals the enumerated maximum."""
+    for rows, cols, W, V in _golden_rows("page_plans.txt"):
+        counts = {}
+        for i in range(cols):
+            wk = (i // V) % W            # owner by counting runs of V across W workers
+            counts[wk] = counts.get(wk, 0) + 1
+        assert oracle.slot_bound(cols, W, V) == max(counts.values())
