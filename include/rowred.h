@@ -1,0 +1,189 @@
+/*
+ * rowred.h — FP32 row reductions for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * Every operator reduces each row of a row-major, contiguous float32 matrix
+ * x[rows][cols] independently. Sources of the definitions:
+ *   - RMSNorm and its calling convention (input, weight, output, eps; rows*cols
+ *     inputs and outputs, cols weights; 0 < cols; FP32 reduction and epilogue
+ *     with rounding only on the output store): meTile, "Thread Ownership and
+ *     Software Staging", section "Register-tiled reductions" (the register
+ *     RMSNorm kernel's contract).
+ *   - The sibling operators (row sum, softmax, LayerNorm, residual LayerNorm,
+ *     cross-entropy) on one reduction core: LuisaCompute notes, "Consecutive-
+ *     worker reduction layout checkpoint", section "Evidence and what remains"
+ *     (the operator-coverage item). Their formulas are the textbook ones and
+ *     are stated on each declaration below.
+ *   - The worker / V ownership map behind rr_plan: same LuisaCompute page,
+ *     section "Implementation and semantics".
+ *   - Fail-closed geometry (an illegal plan is rejected, never remapped):
+ *     meTile page above, section "Compiler-selected communication" (the
+ *     thread-limit check), and the LuisaCompute page, section "Verification
+ *     checkpoint" (invalid widths and resource overflow fail closed).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers (hipMalloc / PyTorch CUDA tensors) owned by
+ *     the caller; all tensors are contiguous row-major float32 (targets int32),
+ *     at least 4-byte aligned. Outputs are preallocated by the caller.
+ *   - The library allocates nothing, frees nothing and never synchronises: it
+ *     enqueues one kernel on `stream` (a hipStream_t; NULL = the default
+ *     stream) and returns. Faults during execution surface at the caller's
+ *     next synchronisation.
+ *   - y may alias x exactly (in-place); any other overlap between an output
+ *     and an input is undefined.
+ *   - Return value is an rr_status. rows == 0 returns RR_OK without touching
+ *     the GPU. rows < 0, cols <= 0, a NULL required pointer (when rows > 0), a
+ *     pointer not 4-byte aligned, or an eps that is negative or not finite
+ *     return RR_ERR_INVALID_ARGUMENT. cols > 2^31-1, a grid beyond the device
+ *     limit, or an explicit plan that is illegal for (op, rows, cols) return
+ *     RR_ERR_UNSUPPORTED. A launch the HIP runtime refuses returns
+ *     RR_ERR_LAUNCH. Nothing is enqueued unless RR_OK is returned.
+ *   - No global mutable state: all entry points are reentrant and may be
+ *     called concurrently from several host threads.
+ *   - Arithmetic is float32 (row sum: float64 accumulation, see below); the
+ *     order of additions inside a row depends on the plan, as the ownership
+ *     map permits.
+ */
+#ifndef ROWRED_H
+#define ROWRED_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rr_status {
+    RR_OK = 0,
+    RR_ERR_INVALID_ARGUMENT = 1,
+    RR_ERR_UNSUPPORTED = 2,
+    RR_ERR_LAUNCH = 3
+} rr_status;
+
+typedef enum rr_op {
+    RR_OP_RMSNORM = 0,
+    RR_OP_SUM = 1,
+    RR_OP_SOFTMAX = 2,
+    RR_OP_LAYERNORM = 3,
+    RR_OP_RESIDUAL_LAYERNORM = 4,
+    RR_OP_CROSS_ENTROPY = 5
+} rr_op;
+
+/* How rows map onto workgroups.
+ *   RR_PATH_PACKED: lanes_per_row < 64 — several rows share one 64-lane
+ *                   wavefront; each row is reduced inside its lane segment.
+ *   RR_PATH_ROW:    lanes_per_row >= 64 — one row spans lanes_per_row/64 whole
+ *                   wavefronts (combined through LDS with one barrier per
+ *                   reduction); a workgroup may hold several rows.
+ *   RR_PATH_LOOP:   one row per workgroup, values are re-read from memory
+ *                   instead of kept in registers; any cols. */
+typedef enum rr_path {
+    RR_PATH_PACKED = 0,
+    RR_PATH_ROW = 1,
+    RR_PATH_LOOP = 2
+} rr_path;
+
+/* A launch plan. Worker w (0 <= w < lanes_per_row) of a row owns logical
+ * columns i = (chunk * lanes_per_row + w) * v + e for 0 <= e < v, and keeps
+ * them in private slot chunk * v + e (LuisaCompute page, section
+ * "Implementation and semantics").
+ *   path            rr_path
+ *   block           threads per workgroup: 64, 128, 256, 512 or 1024
+ *   lanes_per_row   workers per row: power of two, 8..1024, <= block
+ *                   (LOOP: equal to block)
+ *   rows_per_group  block / lanes_per_row (LOOP: 1)
+ *   v               consecutive floats per worker pack: 1, 2 or 4
+ *   slots           floats each worker keeps in registers: chunks * v with
+ *                   chunks in {1, 2, 4, 8}; cols <= lanes_per_row * slots.
+ *                   0 on the LOOP path. */
+typedef struct rr_plan {
+    int32_t path;
+    int32_t block;
+    int32_t lanes_per_row;
+    int32_t rows_per_group;
+    int32_t v;
+    int32_t slots;
+} rr_plan;
+
+/* RMSNorm: y[r,c] = x[r,c] * w[c] / sqrt(mean_c x[r,c]^2 + eps).
+ * x, y: rows*cols floats; w: cols floats. */
+int rmsnorm_f32(const float *x, const float *w, float *y,
+                int64_t rows, int64_t cols, float eps, void *stream);
+
+/* Row sum: out[r] = sum_c x[r,c]. Accumulates in float64 and rounds once,
+ * so the result is within float32 rounding of the exact sum even when
+ * positive and negative terms cancel. out: rows floats. */
+int row_sum_f32(const float *x, float *out, int64_t rows, int64_t cols, void *stream);
+
+/* Softmax with the row maximum subtracted:
+ * y[r,c] = exp(x[r,c] - m_r) / sum_k exp(x[r,k] - m_r), m_r = max_k x[r,k]. */
+int softmax_f32(const float *x, float *y, int64_t rows, int64_t cols, void *stream);
+
+/* LayerNorm: y = (x - mean_r) / sqrt(var_r + eps) * gamma[c] + beta[c], with
+ * the population variance var_r = mean_c (x[r,c] - mean_r)^2 (two passes over
+ * the register-resident row). gamma, beta: cols floats. */
+int layernorm_f32(const float *x, const float *gamma, const float *beta, float *y,
+                  int64_t rows, int64_t cols, float eps, void *stream);
+
+/* Residual LayerNorm: h = x + residual rounded to float32, then LayerNorm of h.
+ * h_out may be NULL; otherwise it receives h (rows*cols floats, bit-exact
+ * float32 sums). */
+int residual_layernorm_f32(const float *x, const float *residual,
+                           const float *gamma, const float *beta,
+                           float *y, float *h_out,
+                           int64_t rows, int64_t cols, float eps, void *stream);
+
+/* Cross-entropy per row with int32 class targets:
+ * loss[r] = log sum_c exp(x[r,c] - m_r) + m_r - x[r, targets[r]].
+ * Targets are not validated on the host (that would need a synchronisation):
+ * a target outside [0, cols) yields loss = NaN and no out-of-bounds read.
+ * targets, loss: rows elements. */
+int cross_entropy_f32(const float *logits, const int32_t *targets, float *loss,
+                      int64_t rows, int64_t cols, void *stream);
+
+/* Explicit-plan forms. plan == NULL selects the plan as the plain forms do;
+ * otherwise the plan must be legal for (op, rows, cols) — checked exactly as
+ * rr_check_plan does — or RR_ERR_UNSUPPORTED is returned. */
+int rmsnorm_f32_ex(const float *x, const float *w, float *y,
+                   int64_t rows, int64_t cols, float eps, const rr_plan *plan, void *stream);
+int row_sum_f32_ex(const float *x, float *out, int64_t rows, int64_t cols,
+                   const rr_plan *plan, void *stream);
+int softmax_f32_ex(const float *x, float *y, int64_t rows, int64_t cols,
+                   const rr_plan *plan, void *stream);
+int layernorm_f32_ex(const float *x, const float *gamma, const float *beta, float *y,
+                     int64_t rows, int64_t cols, float eps, const rr_plan *plan, void *stream);
+int residual_layernorm_f32_ex(const float *x, const float *residual,
+                              const float *gamma, const float *beta,
+                              float *y, float *h_out, int64_t rows, int64_t cols, float eps,
+                              const rr_plan *plan, void *stream);
+int cross_entropy_f32_ex(const float *logits, const int32_t *targets, float *loss,
+                         int64_t rows, int64_t cols, const rr_plan *plan, void *stream);
+
+/* Plan the library would use for (op, rows, cols): the measured per-shape
+ * table entry when one exists, else the built-in rule. Pure host function;
+ * no GPU needed. Returns RR_ERR_INVALID_ARGUMENT for an unknown op, rows < 0,
+ * cols <= 0 or out == NULL, RR_ERR_UNSUPPORTED for cols > 2^31-1. */
+int rr_select_plan(int op, int64_t rows, int64_t cols, rr_plan *out);
+
+/* RR_OK if `plan` is legal for (op, rows, cols), else RR_ERR_UNSUPPORTED
+ * (RR_ERR_INVALID_ARGUMENT for bad op / shape / NULL plan). Pure host. */
+int rr_check_plan(int op, int64_t rows, int64_t cols, const rr_plan *plan);
+
+/* Static, NUL-terminated name of a status code. */
+const char *rr_status_string(int status);
+
+/* ---- Measurement helpers (not part of the method) ------------------------
+ * Used by the benchmark to put the operators next to a plain streaming copy
+ * of known size (HBM ceiling, counter calibration) and an empty kernel
+ * (launch floor). Same ownership and error conventions as above. */
+
+/* dst[i] = src[i] for 0 <= i < n (n floats; no overlap). */
+int rr_copy_f32(const float *src, float *dst, int64_t n, void *stream);
+
+/* Launches one workgroup of one wavefront that does nothing. */
+int rr_empty_kernel(void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROWRED_H */

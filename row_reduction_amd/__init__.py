@@ -1,0 +1,195 @@
+"""FP32 row reductions on AMD Instinct MI355X (gfx950) — Python binding.
+
+Thin wrappers over the C entry points of ``librowred.so`` (declared in
+``include/rowred.h``) with the same names. They only marshal arguments:
+check that tensors are contiguous float32 (int32 targets) on a GPU, pass
+``data_ptr()`` values, the shape, and the current HIP stream, and allocate
+outputs the caller did not supply. Every operator runs in the library's HIP
+kernels; nothing here computes.
+
+Importing this package does not load the library; the first call does, and
+raises RuntimeError if it has not been built.
+"""
+from __future__ import annotations
+
+from . import _capi
+from ._capi import OP_IDS, RowRedError, rr_plan
+
+__all__ = [
+    "rmsnorm_f32", "row_sum_f32", "softmax_f32", "layernorm_f32",
+    "residual_layernorm_f32", "cross_entropy_f32",
+    "rr_select_plan", "rr_check_plan", "rr_status_string", "rr_copy_f32", "rr_empty_kernel",
+    "rr_plan", "RowRedError", "OP_IDS",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    if stream is not None:
+        return int(stream)
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _mat(t, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda:
+        raise TypeError(f"{name} must be a float32 CUDA/HIP tensor")
+    if t.dim() != 2 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 2-d tensor, got shape {tuple(t.shape)}")
+    return t
+
+
+def _vec(t, n, name, dtype=None):
+    torch = _torch()
+    dtype = dtype or torch.float32
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
+        raise TypeError(f"{name} must be a {dtype} CUDA/HIP tensor")
+    if t.dim() != 1 or t.numel() != n or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous with {n} elements, got shape {tuple(t.shape)}")
+    return t
+
+
+def _out_like(out, x, name):
+    if out is None:
+        return _torch().empty_like(x)
+    _mat(out, name)
+    if out.shape != x.shape:
+        raise ValueError(f"{name} must have shape {tuple(x.shape)}")
+    return out
+
+
+def _out_rows(out, x, name):
+    torch = _torch()
+    if out is None:
+        return torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
+    return _vec(out, x.shape[0], name)
+
+
+def _plan_ptr(plan):
+    if plan is None:
+        return None
+    if isinstance(plan, dict):
+        plan = rr_plan.from_dict(plan)
+    return plan
+
+
+def rmsnorm_f32(x, w, eps=1e-6, y=None, plan=None, stream=None):
+    """y[r,c] = x[r,c] * w[c] / sqrt(mean_c x[r,c]^2 + eps). Returns y."""
+    _mat(x, "x")
+    rows, cols = x.shape
+    _vec(w, cols, "w")
+    y = _out_like(y, x, "y")
+    st = _capi.lib().rmsnorm_f32_ex(x.data_ptr(), w.data_ptr(), y.data_ptr(), rows, cols, float(eps),
+                                     _plan_ptr(plan), _stream(stream))
+    _capi.check("rmsnorm_f32", st)
+    return y
+
+
+def row_sum_f32(x, out=None, plan=None, stream=None):
+    """out[r] = sum_c x[r,c] (float64 accumulation, one rounding). Returns out."""
+    _mat(x, "x")
+    rows, cols = x.shape
+    out = _out_rows(out, x, "out")
+    st = _capi.lib().row_sum_f32_ex(x.data_ptr(), out.data_ptr(), rows, cols, _plan_ptr(plan),
+                                     _stream(stream))
+    _capi.check("row_sum_f32", st)
+    return out
+
+
+def softmax_f32(x, y=None, plan=None, stream=None):
+    """Row softmax with the row maximum subtracted. Returns y."""
+    _mat(x, "x")
+    rows, cols = x.shape
+    y = _out_like(y, x, "y")
+    st = _capi.lib().softmax_f32_ex(x.data_ptr(), y.data_ptr(), rows, cols, _plan_ptr(plan),
+                                     _stream(stream))
+    _capi.check("softmax_f32", st)
+    return y
+
+
+def layernorm_f32(x, gamma, beta, eps=1e-5, y=None, plan=None, stream=None):
+    """y = (x - mean) / sqrt(var + eps) * gamma + beta per row. Returns y."""
+    _mat(x, "x")
+    rows, cols = x.shape
+    _vec(gamma, cols, "gamma")
+    _vec(beta, cols, "beta")
+    y = _out_like(y, x, "y")
+    st = _capi.lib().layernorm_f32_ex(x.data_ptr(), gamma.data_ptr(), beta.data_ptr(), y.data_ptr(),
+                                       rows, cols, float(eps), _plan_ptr(plan), _stream(stream))
+    _capi.check("layernorm_f32", st)
+    return y
+
+
+def residual_layernorm_f32(x, residual, gamma, beta, eps=1e-5, y=None, h_out=None, plan=None,
+                           stream=None):
+    """h = x + residual (float32); y = LayerNorm(h). Writes h to h_out when given. Returns y."""
+    _mat(x, "x")
+    rows, cols = x.shape
+    _mat(residual, "residual")
+    if residual.shape != x.shape:
+        raise ValueError("residual must have the shape of x")
+    _vec(gamma, cols, "gamma")
+    _vec(beta, cols, "beta")
+    y = _out_like(y, x, "y")
+    h_ptr = None
+    if h_out is not None:
+        _out_like(h_out, x, "h_out")
+        h_ptr = h_out.data_ptr()
+    st = _capi.lib().residual_layernorm_f32_ex(x.data_ptr(), residual.data_ptr(), gamma.data_ptr(),
+                                                beta.data_ptr(), y.data_ptr(), h_ptr, rows, cols,
+                                                float(eps), _plan_ptr(plan), _stream(stream))
+    _capi.check("residual_layernorm_f32", st)
+    return y
+
+
+def cross_entropy_f32(logits, targets, loss=None, plan=None, stream=None):
+    """loss[r] = logsumexp_c logits[r,c] - logits[r, targets[r]]. Returns loss."""
+    torch = _torch()
+    _mat(logits, "logits")
+    rows, cols = logits.shape
+    _vec(targets, rows, "targets", dtype=torch.int32)
+    loss = _out_rows(loss, logits, "loss")
+    st = _capi.lib().cross_entropy_f32_ex(logits.data_ptr(), targets.data_ptr(), loss.data_ptr(),
+                                           rows, cols, _plan_ptr(plan), _stream(stream))
+    _capi.check("cross_entropy_f32", st)
+    return loss
+
+
+def rr_select_plan(op, rows, cols) -> rr_plan:
+    """Plan the library picks for (op, rows, cols); op is a name or an rr_op value."""
+    op_id = OP_IDS[op] if isinstance(op, str) else int(op)
+    p = rr_plan()
+    _capi.check("rr_select_plan", _capi.lib().rr_select_plan(op_id, rows, cols, p))
+    return p
+
+
+def rr_check_plan(op, rows, cols, plan) -> int:
+    """rr_status of the legality check of `plan` for (op, rows, cols)."""
+    op_id = OP_IDS[op] if isinstance(op, str) else int(op)
+    return _capi.lib().rr_check_plan(op_id, rows, cols, _plan_ptr(plan))
+
+
+def rr_status_string(status: int) -> str:
+    return _capi.status_string(status)
+
+
+def rr_copy_f32(src, dst, stream=None):
+    """dst[:] = src[:] through the library's streaming copy kernel."""
+    torch = _torch()
+    for t, n in ((src, "src"), (dst, "dst")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda \
+                or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous float32 CUDA/HIP tensor")
+    if src.numel() != dst.numel():
+        raise ValueError("src and dst sizes differ")
+    _capi.check("rr_copy_f32", _capi.lib().rr_copy_f32(src.data_ptr(), dst.data_ptr(), src.numel(),
+                                                        _stream(stream)))
+    return dst
+
+
+def rr_empty_kernel(stream=None):
+    _capi.check("rr_empty_kernel", _capi.lib().rr_empty_kernel(_stream(stream)))

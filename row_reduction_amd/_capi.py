@@ -1,0 +1,128 @@
+"""ctypes view of librowred.so: the C entry points declared in include/rowred.h.
+
+Loading fails loudly (RuntimeError) when the library has not been built;
+there is no fallback implementation of any operator.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librowred.so")
+
+RR_OK = 0
+RR_ERR_INVALID_ARGUMENT = 1
+RR_ERR_UNSUPPORTED = 2
+RR_ERR_LAUNCH = 3
+
+RR_OP_RMSNORM = 0
+RR_OP_SUM = 1
+RR_OP_SOFTMAX = 2
+RR_OP_LAYERNORM = 3
+RR_OP_RESIDUAL_LAYERNORM = 4
+RR_OP_CROSS_ENTROPY = 5
+
+RR_PATH_PACKED = 0
+RR_PATH_ROW = 1
+RR_PATH_LOOP = 2
+
+OP_IDS = {
+    "rmsnorm": RR_OP_RMSNORM,
+    "sum": RR_OP_SUM,
+    "softmax": RR_OP_SOFTMAX,
+    "layernorm": RR_OP_LAYERNORM,
+    "residual_layernorm": RR_OP_RESIDUAL_LAYERNORM,
+    "cross_entropy": RR_OP_CROSS_ENTROPY,
+}
+
+# Every symbol include/rowred.h declares.
+EXPORTED = (
+    "rmsnorm_f32", "row_sum_f32", "softmax_f32", "layernorm_f32",
+    "residual_layernorm_f32", "cross_entropy_f32",
+    "rmsnorm_f32_ex", "row_sum_f32_ex", "softmax_f32_ex", "layernorm_f32_ex",
+    "residual_layernorm_f32_ex", "cross_entropy_f32_ex",
+    "rr_select_plan", "rr_check_plan", "rr_status_string",
+    "rr_copy_f32", "rr_empty_kernel",
+)
+
+
+class rr_plan(ctypes.Structure):
+    _fields_ = [
+        ("path", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("lanes_per_row", ctypes.c_int32),
+        ("rows_per_group", ctypes.c_int32),
+        ("v", ctypes.c_int32),
+        ("slots", ctypes.c_int32),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+    @classmethod
+    def from_dict(cls, d: dict) -> "rr_plan":
+        return cls(**{name: int(d[name]) for name, _ in cls._fields_})
+
+    def __repr__(self) -> str:
+        return f"rr_plan({self.as_dict()})"
+
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_planp = ctypes.POINTER(rr_plan)
+
+_SIGNATURES = {
+    "rmsnorm_f32": [_vp, _vp, _vp, _i64, _i64, _f32, _vp],
+    "row_sum_f32": [_vp, _vp, _i64, _i64, _vp],
+    "softmax_f32": [_vp, _vp, _i64, _i64, _vp],
+    "layernorm_f32": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp],
+    "residual_layernorm_f32": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp],
+    "cross_entropy_f32": [_vp, _vp, _vp, _i64, _i64, _vp],
+    "rmsnorm_f32_ex": [_vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp],
+    "row_sum_f32_ex": [_vp, _vp, _i64, _i64, _planp, _vp],
+    "softmax_f32_ex": [_vp, _vp, _i64, _i64, _planp, _vp],
+    "layernorm_f32_ex": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp],
+    "residual_layernorm_f32_ex": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp],
+    "cross_entropy_f32_ex": [_vp, _vp, _vp, _i64, _i64, _planp, _vp],
+    "rr_select_plan": [ctypes.c_int, _i64, _i64, _planp],
+    "rr_check_plan": [ctypes.c_int, _i64, _i64, _planp],
+    "rr_status_string": [ctypes.c_int],
+    "rr_copy_f32": [_vp, _vp, _i64, _vp],
+    "rr_empty_kernel": [_vp],
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded once). Raises RuntimeError if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+                "or `python row_reduction_amd/build.py` first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, argtypes in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = argtypes
+            fn.restype = ctypes.c_char_p if name == "rr_status_string" else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().rr_status_string(code).decode()
+
+
+class RowRedError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+
+
+def check(fn: str, status: int) -> None:
+    if status != RR_OK:
+        raise RowRedError(fn, status)

@@ -1,0 +1,95 @@
+"""Build librowred.so (HIP for gfx950) in-tree.
+
+Each translation unit compiles in its own hipcc process (in parallel), then
+one link step produces ``row_reduction_amd/librowred.so``. Objects go to
+``row_reduction_amd/_build/`` (not committed).
+
+Device code is built with packed-FP32 instruction selection turned off
+(``-target-feature -packed-fp32-ops``); hipcc's host pass warns that it does
+not know that feature, which is expected.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "librowred.so")
+
+ARCH = "gfx950"
+HIP_SOURCES = [
+    "api.hip",
+    "measure.hip",
+    "kernels_rmsnorm.hip",
+    "kernels_row_sum.hip",
+    "kernels_softmax.hip",
+    "kernels_layernorm.hip",
+    "kernels_residual_layernorm.hip",
+    "kernels_cross_entropy.hip",
+]
+CXX_SOURCES = ["plan.cpp"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build librowred)")
+
+
+def hip_flags() -> list[str]:
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function",
+        f"-I{INCLUDE}", f"-I{CSRC}",
+    ]
+
+
+def _run(cmd: list[str]) -> None:
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # The host pass's notice about the device-only feature is expected noise.
+    lines = [ln for ln in proc.stdout.splitlines()
+             if "packed-fp32-ops' is not a recognized feature" not in ln]
+    if proc.returncode != 0:
+        raise RuntimeError("command failed:\n  " + " ".join(cmd) + "\n" + "\n".join(lines))
+    if lines:
+        sys.stderr.write("\n".join(lines) + "\n")
+
+
+def build(jobs: int | None = None, verbose: bool = False) -> str:
+    """Compile every source and link librowred.so; returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    cmds = []
+    objs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([cc, *hip_flags(), "-c", os.path.join(CSRC, src), "-o", obj])
+    for src in CXX_SOURCES:
+        obj = os.path.join(BUILD, src.replace(".cpp", ".o"))
+        objs.append(obj)
+        cmds.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}",
+                     "-I/opt/rocm/include", "-c", os.path.join(CSRC, src), "-o", obj])
+    jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 4)), 16)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        for fut in [ex.submit(_run, c) for c in cmds]:
+            fut.result()
+    tmp = LIB + f".tmp{os.getpid()}"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,602 @@
+// Device side of librowred: the shared row-reduction core and the per-operator
+// epilogues, written for gfx950 (CDNA4, 64-lane wavefronts).
+//
+// One worker (lane) of a row owns columns i = (chunk * W + w) * V + e and keeps
+// them in private slot chunk * V + e (LuisaCompute notes, "Consecutive-worker
+// reduction layout checkpoint", section "Implementation and semantics").
+// The same map serves the load, the reduction and the store. When the row is
+// an exact multiple of the plan's span every pack is one V-wide access;
+// otherwise each pack loads the in-bounds V-wide window nearest to it and
+// selects its columns, so no load is guarded by a branch, and stores of the
+// one partial pack per worker are guarded element by element. Nothing is read
+// or written past the row (meTile "Thread Ownership and Software Staging",
+// section "Contiguous register memory": no speculative access beyond a ragged
+// tensor).
+//
+// A row's partials combine in three levels, each in a fixed order so results
+// are reproducible run to run:
+//   1. a balanced tree over the worker's own slots (meTile page, section
+//      "Register-tiled reductions");
+//   2. a butterfly inside the row's lane segment of the wavefront: DPP
+//      quad permutes and mirrors for distances 1..8, ds_swizzle for 16 and
+//      two readlanes for 32 — every lane ends with the same value;
+//   3. when a row spans several wavefronts, one float per wavefront in LDS,
+//      one barrier, and every wavefront summing all partials itself (meTile
+//      page, same section: private reduction scratch needs one barrier;
+//      each sequential reduction gets its own scratch).
+// Every lane takes part in every reduction; lanes without data contribute the
+// operation's identity.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace rowred {
+
+enum OpId { kRmsNorm = 0, kSum = 1, kSoftmax = 2, kLayerNorm = 3, kResidualLayerNorm = 4, kCrossEntropy = 5 };
+
+// V consecutive floats at 4-byte alignment. Row origins of odd-width rows are
+// only dword aligned; gfx9 vector memory instructions accept that.
+typedef float f32x2u __attribute__((ext_vector_type(2), aligned(4)));
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+
+template <int V>
+__device__ __forceinline__ void load_pack(const float *__restrict__ p, float *d) {
+    if constexpr (V == 1) {
+        d[0] = p[0];
+    } else if constexpr (V == 2) {
+        f32x2u t = *reinterpret_cast<const f32x2u *>(p);
+        d[0] = t.x;
+        d[1] = t.y;
+    } else {
+        static_assert(V == 4, "V must be 1, 2 or 4");
+        f32x4u t = *reinterpret_cast<const f32x4u *>(p);
+        d[0] = t.x;
+        d[1] = t.y;
+        d[2] = t.z;
+        d[3] = t.w;
+    }
+}
+
+template <int V>
+__device__ __forceinline__ void store_pack(float *__restrict__ p, const float *d) {
+    if constexpr (V == 1) {
+        p[0] = d[0];
+    } else if constexpr (V == 2) {
+        f32x2u t;
+        t.x = d[0];
+        t.y = d[1];
+        *reinterpret_cast<f32x2u *>(p) = t;
+    } else {
+        f32x4u t;
+        t.x = d[0];
+        t.y = d[1];
+        t.z = d[2];
+        t.w = d[3];
+        *reinterpret_cast<f32x4u *>(p) = t;
+    }
+}
+
+// Pack of V columns starting at i0 of a row with `cols` columns (cols >= V),
+// without branches: the V-wide load always reads the in-bounds window that
+// starts at min(i0, cols - V), and each slot then picks its column out of
+// the window, or `fill` when the column lies past the row end. A complete
+// pack reads exactly its own columns; nothing outside the row is read.
+template <int V>
+__device__ __forceinline__ void load_window(const float *__restrict__ row, int i0, int cols, float *d,
+                                            float fill) {
+    if constexpr (V == 1) {
+        const float t = row[i0 < cols ? i0 : cols - 1];
+        d[0] = (i0 < cols) ? t : fill;
+    } else {
+        const int start = i0 < cols - V ? i0 : cols - V;
+        const int shift = i0 - start;  // 0 for a complete pack
+        float t[V];
+        load_pack<V>(row + start, t);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const int p = e + shift;
+            float s = fill;
+#pragma unroll
+            for (int q = V - 1; q >= 0; --q) s = (p == q) ? t[q] : s;
+            d[e] = s;
+        }
+    }
+}
+
+// Store of the columns of a pack that lie inside the row.
+template <int V>
+__device__ __forceinline__ void store_guarded(float *__restrict__ row, int i0, int cols, const float *d) {
+    if (i0 + V <= cols) {
+        store_pack<V>(row + i0, d);
+    } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            if (i0 + e < cols) row[i0 + e] = d[e];
+    }
+}
+
+// Load / store of one pack: plain V-wide access when the row is an exact
+// multiple of the plan's span (every pack complete), else the guarded forms.
+template <int V, bool EXACT>
+__device__ __forceinline__ void load_slots(const float *__restrict__ row, int i0, int cols, float *d,
+                                           float fill) {
+    if constexpr (EXACT) load_pack<V>(row + i0, d);
+    else load_window<V>(row, i0, cols, d, fill);
+}
+
+template <int V, bool EXACT>
+__device__ __forceinline__ void store_slots(float *__restrict__ row, int i0, int cols, const float *d) {
+    if constexpr (EXACT) store_pack<V>(row + i0, d);
+    else store_guarded<V>(row, i0, cols, d);
+}
+
+// ---- combine operations ------------------------------------------------------
+
+struct AddOp {
+    template <class T>
+    __device__ __forceinline__ T operator()(T a, T b) const { return a + b; }
+};
+struct MaxOp {
+    __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+// Balanced tree over K (a power of two) values; overwrites t.
+template <int K, class T, class Op>
+__device__ __forceinline__ T tree_reduce(T *t, Op op) {
+#pragma unroll
+    for (int s = K / 2; s > 0; s /= 2) {
+#pragma unroll
+        for (int k = 0; k < s; ++k) t[k] = op(t[k], t[k + s]);
+    }
+    return t[0];
+}
+
+// ---- cross-lane moves ------------------------------------------------------------
+
+// DPP controls: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
+// row_half_mirror (lane i of 8 reads 7 - i), row_mirror (lane i of 16 reads 15 - i).
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+// ds_swizzle bit-mask mode: and 0x1f, or 0, xor 0x10 (lane ^ 16 inside 32).
+constexpr int kSwizzleXor16 = (0x10 << 10) | 0x1f;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xf, 0xf, false));
+}
+__device__ __forceinline__ float swizzle_xor16(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), kSwizzleXor16));
+}
+__device__ __forceinline__ float readlane(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// float64 values move as two 32-bit halves.
+struct Halves {
+    int lo, hi;
+};
+__device__ __forceinline__ Halves split(double v) {
+    unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    return Halves{(int)(u & 0xffffffffull), (int)(u >> 32)};
+}
+__device__ __forceinline__ double join(int lo, int hi) {
+    unsigned long long u = ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
+    return __builtin_bit_cast(double, u);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {
+    Halves h = split(v);
+    return join(__builtin_amdgcn_update_dpp(0, h.lo, CTRL, 0xf, 0xf, false),
+                __builtin_amdgcn_update_dpp(0, h.hi, CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ double swizzle_xor16(double v) {
+    Halves h = split(v);
+    return join(__builtin_amdgcn_ds_swizzle(h.lo, kSwizzleXor16),
+                __builtin_amdgcn_ds_swizzle(h.hi, kSwizzleXor16));
+}
+__device__ __forceinline__ double readlane(double v, int lane) {
+    Halves h = split(v);
+    return join(__builtin_amdgcn_readlane(h.lo, lane), __builtin_amdgcn_readlane(h.hi, lane));
+}
+
+// Butterfly over aligned segments of SEG lanes (8, 16, 32 or 64). All lanes
+// must be active. Afterwards every lane of a segment holds the same value:
+// each step combines a lane with a partner holding the complementary half
+// and the operations are commutative.
+template <int SEG, class T, class Op>
+__device__ __forceinline__ T segment_reduce(T v, Op op) {
+    static_assert(SEG == 8 || SEG == 16 || SEG == 32 || SEG == 64, "segment of 8..64 lanes");
+    v = op(v, dpp<kDppXor1>(v));
+    v = op(v, dpp<kDppXor2>(v));
+    v = op(v, dpp<kDppHalfMirror>(v));
+    if constexpr (SEG >= 16) v = op(v, dpp<kDppMirror>(v));
+    if constexpr (SEG >= 32) v = op(v, swizzle_xor16(v));
+    if constexpr (SEG >= 64) v = op(readlane(v, 0), readlane(v, 32));
+    return v;
+}
+
+// Lanes of one row and where they sit in the workgroup.
+template <int SEG>
+struct RowLanes {
+    int W;            // workers per row
+    int lane;         // worker index inside the row
+    int row_in_group; // which of the group's rows
+    int wave;         // wavefront index inside the group
+    int first_wave;   // first wavefront of this row (ROW path)
+    int waves;        // wavefronts per row (ROW path)
+
+    __device__ __forceinline__ explicit RowLanes(const Args &a) {
+        const int tid = threadIdx.x;
+        if constexpr (SEG < 64) {
+            W = SEG;
+            lane = tid & (SEG - 1);
+            row_in_group = tid / SEG;
+            waves = 1;
+        } else {
+            W = a.lanes_per_row;
+            lane = tid & (W - 1);
+            row_in_group = tid >> a.log2_lanes;
+            waves = W >> 6;
+        }
+        wave = tid >> 6;
+        first_wave = row_in_group * waves;
+    }
+};
+
+// Full row reduction: segment butterfly, then (rows wider than a wavefront)
+// one partial per wavefront through `lds`, one barrier, fixed-order sum.
+template <int SEG, class T, class Op>
+__device__ __forceinline__ T row_reduce(T v, Op op, const RowLanes<SEG> &rl, T *lds) {
+    v = segment_reduce<(SEG < 64 ? SEG : 64)>(v, op);
+    if constexpr (SEG == 64) {
+        if (rl.waves > 1) {
+            if ((threadIdx.x & 63) == 0) lds[rl.wave] = v;
+            __syncthreads();
+            T acc = lds[rl.first_wave];
+            for (int j = 1; j < rl.waves; ++j) acc = op(acc, lds[rl.first_wave + j]);
+            v = acc;
+        }
+    }
+    return v;
+}
+
+// ---- register-resident kernel ---------------------------------------------------
+//
+// OP: operator; V: floats per pack; NCHUNK: packs per worker (K = V*NCHUNK
+// live floats); SEG: lanes per row when < 64 (several rows per wavefront), or
+// 64 when a row takes lanes_per_row / 64 whole wavefronts; EXACT: the row
+// length equals lanes_per_row * K, so every pack is complete.
+template <int OP, int V, int NCHUNK, int SEG, bool EXACT>
+__global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
+    constexpr int K = V * NCHUNK;
+    constexpr bool kMaxFirst = (OP == kSoftmax || OP == kCrossEntropy);
+    __shared__ float lds0[16];
+    __shared__ float lds1[16];
+    __shared__ double ldsd[16];
+
+    const RowLanes<SEG> rl(a);
+    const int cols = a.cols;
+    const int64_t row_raw = (int64_t)blockIdx.x * a.rows_per_group + rl.row_in_group;
+    const bool row_ok = row_raw < a.rows;
+    // Lanes of a group's missing last rows mirror the final row and store nothing.
+    const int64_t row = row_ok ? row_raw : a.rows - 1;
+    const int64_t off = row * (int64_t)cols;
+    const int stride = rl.W * V;  // columns per chunk
+    const int base = rl.lane * V;
+    const float fill = kMaxFirst ? -INFINITY : 0.0f;
+
+    // Cross-entropy: fetch the target logit early (one dword, no read when
+    // the target is out of range).
+    float x_target = 0.0f;
+    if constexpr (OP == kCrossEntropy) {
+        const int t = a.targets[row];
+        x_target = (t >= 0 && t < cols) ? a.x[off + t] : __builtin_nanf("");
+    }
+
+    // ---- load: the worker's K floats stay in registers until the store.
+    float v[K];
+#pragma unroll
+    for (int c = 0; c < NCHUNK; ++c) load_slots<V, EXACT>(a.x + off, c * stride + base, cols, &v[c * V], fill);
+    if constexpr (OP == kResidualLayerNorm) {
+        float r[K];
+#pragma unroll
+        for (int c = 0; c < NCHUNK; ++c)
+            load_slots<V, EXACT>(a.residual + off, c * stride + base, cols, &r[c * V], 0.0f);
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = v[k] + r[k];
+        if (a.h_out != nullptr && row_ok) {
+#pragma unroll
+            for (int c = 0; c < NCHUNK; ++c) store_slots<V, EXACT>(a.h_out + off, c * stride + base, cols, &v[c * V]);
+        }
+    }
+
+    if constexpr (OP == kRmsNorm) {
+        // The weights are issued with the row so their latency hides behind
+        // the reduction; the epilogue then only multiplies and stores.
+        float wv[K];
+#pragma unroll
+        for (int c = 0; c < NCHUNK; ++c) load_slots<V, EXACT>(a.w, c * stride + base, cols, &wv[c * V], 0.0f);
+        float t[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) t[k] = v[k] * v[k];
+        const float ss = row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds0);
+        const float inv = rsqrtf(ss / (float)cols + a.eps);
+        if (row_ok) {
+#pragma unroll
+            for (int c = 0; c < NCHUNK; ++c) {
+                float o[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) o[e] = v[c * V + e] * inv * wv[c * V + e];
+                store_slots<V, EXACT>(a.y + off, c * stride + base, cols, o);
+            }
+        }
+    } else if constexpr (OP == kSum) {
+        double t[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) t[k] = (double)v[k];
+        const double s = row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, ldsd);
+        if (row_ok && rl.lane == 0) a.row_out[row] = (float)s;
+    } else if constexpr (OP == kSoftmax || OP == kCrossEntropy) {
+        float t[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) t[k] = v[k];
+        const float m = row_reduce(tree_reduce<K>(t, MaxOp{}), MaxOp{}, rl, lds0);
+        // Missing columns hold -inf, so exp gives 0 there.
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = expf(v[k] - m);
+#pragma unroll
+        for (int k = 0; k < K; ++k) t[k] = v[k];
+        const float z = row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds1);
+        if constexpr (OP == kSoftmax) {
+            const float rz = 1.0f / z;
+            if (row_ok) {
+#pragma unroll
+                for (int c = 0; c < NCHUNK; ++c) {
+                    float o[V];
+#pragma unroll
+                    for (int e = 0; e < V; ++e) o[e] = v[c * V + e] * rz;
+                    store_slots<V, EXACT>(a.y + off, c * stride + base, cols, o);
+                }
+            }
+        } else {
+            if (row_ok && rl.lane == 0) a.row_out[row] = logf(z) + m - x_target;
+        }
+    } else {
+        static_assert(OP == kLayerNorm || OP == kResidualLayerNorm, "unknown operator");
+        float t[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) t[k] = v[k];
+        const float mean = row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds0) / (float)cols;
+        // Deviations; slots past the row end must not count in the variance.
+#pragma unroll
+        for (int c = 0; c < NCHUNK; ++c) {
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float d = v[c * V + e] - mean;
+                v[c * V + e] = (EXACT || c * stride + base + e < cols) ? d : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) t[k] = v[k] * v[k];
+        const float var = row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds1) / (float)cols;
+        const float rstd = rsqrtf(var + a.eps);
+        if (row_ok) {
+            // All gamma / beta packs are issued before the first store.
+            float g[K], b[K];
+#pragma unroll
+            for (int c = 0; c < NCHUNK; ++c) {
+                load_slots<V, EXACT>(a.w, c * stride + base, cols, &g[c * V], 0.0f);
+                load_slots<V, EXACT>(a.beta, c * stride + base, cols, &b[c * V], 0.0f);
+            }
+#pragma unroll
+            for (int c = 0; c < NCHUNK; ++c) {
+                float o[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) o[e] = v[c * V + e] * rstd * g[c * V + e] + b[c * V + e];
+                store_slots<V, EXACT>(a.y + off, c * stride + base, cols, o);
+            }
+        }
+    }
+}
+
+// ---- streaming kernel for rows beyond the register budget ------------------------
+//
+// One row per workgroup, W = blockDim.x workers, the same ownership map with as
+// many chunks as the row needs. Every pass re-reads the row from memory, one
+// branch-free window load per pack.
+template <int OP, int V>
+__global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
+    __shared__ float lds0[16];
+    __shared__ float lds1[16];
+    __shared__ double ldsd[16];
+    const RowLanes<64> rl(a);
+    const int cols = a.cols;
+    const int64_t row = blockIdx.x;
+    const int64_t off = row * (int64_t)cols;
+    const int stride = rl.W * V;
+    const int base = rl.lane * V;
+    const int nchunk = (cols + stride - 1) / stride;
+    const float *xr = a.x + off;
+
+    // Pack of the row's values (x, or x + residual for residual LayerNorm).
+    auto read = [&](int i0, float *d, float fill) {
+        load_window<V>(xr, i0, cols, d, fill);
+        if constexpr (OP == kResidualLayerNorm) {
+            float r[V];
+            load_window<V>(a.residual + off, i0, cols, r, 0.0f);
+#pragma unroll
+            for (int e = 0; e < V; ++e) d[e] = d[e] + r[e];
+        }
+    };
+
+    if constexpr (OP == kRmsNorm) {
+        float acc = 0.0f;
+        for (int c = 0; c < nchunk; ++c) {
+            float d[V];
+            read(c * stride + base, d, 0.0f);
+#pragma unroll
+            for (int e = 0; e < V; ++e) d[e] = d[e] * d[e];
+            acc += tree_reduce<V>(d, AddOp{});
+        }
+        const float ss = row_reduce(acc, AddOp{}, rl, lds0);
+        const float inv = rsqrtf(ss / (float)cols + a.eps);
+        for (int c = 0; c < nchunk; ++c) {
+            const int i0 = c * stride + base;
+            float d[V], wv[V];
+            read(i0, d, 0.0f);
+            load_window<V>(a.w, i0, cols, wv, 0.0f);
+#pragma unroll
+            for (int e = 0; e < V; ++e) d[e] = d[e] * inv * wv[e];
+            store_guarded<V>(a.y + off, i0, cols, d);
+        }
+    } else if constexpr (OP == kSum) {
+        double acc = 0.0;
+        for (int c = 0; c < nchunk; ++c) {
+            float d[V];
+            read(c * stride + base, d, 0.0f);
+            double t[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) t[e] = (double)d[e];
+            acc += tree_reduce<V>(t, AddOp{});
+        }
+        const double s = row_reduce(acc, AddOp{}, rl, ldsd);
+        if (rl.lane == 0) a.row_out[row] = (float)s;
+    } else if constexpr (OP == kSoftmax || OP == kCrossEntropy) {
+        float mx = -INFINITY;
+        for (int c = 0; c < nchunk; ++c) {
+            float d[V];
+            read(c * stride + base, d, -INFINITY);
+            mx = fmaxf(mx, tree_reduce<V>(d, MaxOp{}));
+        }
+        const float m = row_reduce(mx, MaxOp{}, rl, lds0);
+        float acc = 0.0f;
+        for (int c = 0; c < nchunk; ++c) {
+            float d[V];
+            read(c * stride + base, d, -INFINITY);
+#pragma unroll
+            for (int e = 0; e < V; ++e) d[e] = expf(d[e] - m);
+            acc += tree_reduce<V>(d, AddOp{});
+        }
+        const float z = row_reduce(acc, AddOp{}, rl, lds1);
+        if constexpr (OP == kSoftmax) {
+            const float rz = 1.0f / z;
+            for (int c = 0; c < nchunk; ++c) {
+                const int i0 = c * stride + base;
+                float d[V];
+                read(i0, d, -INFINITY);
+#pragma unroll
+                for (int e = 0; e < V; ++e) d[e] = expf(d[e] - m) * rz;
+                store_guarded<V>(a.y + off, i0, cols, d);
+            }
+        } else {
+            if (rl.lane == 0) {
+                const int t = a.targets[row];
+                const float xt = (t >= 0 && t < cols) ? xr[t] : __builtin_nanf("");
+                a.row_out[row] = logf(z) + m - xt;
+            }
+        }
+    } else {
+        static_assert(OP == kLayerNorm || OP == kResidualLayerNorm, "unknown operator");
+        float acc = 0.0f;
+        for (int c = 0; c < nchunk; ++c) {
+            float d[V];
+            read(c * stride + base, d, 0.0f);
+            acc += tree_reduce<V>(d, AddOp{});
+        }
+        const float mean = row_reduce(acc, AddOp{}, rl, lds0) / (float)cols;
+        float acc2 = 0.0f;
+        for (int c = 0; c < nchunk; ++c) {
+            const int i0 = c * stride + base;
+            float d[V];
+            read(i0, d, 0.0f);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float dv = d[e] - mean;
+                d[e] = (i0 + e < cols) ? dv * dv : 0.0f;
+            }
+            acc2 += tree_reduce<V>(d, AddOp{});
+        }
+        const float var = row_reduce(acc2, AddOp{}, rl, lds1) / (float)cols;
+        const float rstd = rsqrtf(var + a.eps);
+        float *hr = (OP == kResidualLayerNorm && a.h_out != nullptr) ? a.h_out + off : nullptr;
+        for (int c = 0; c < nchunk; ++c) {
+            const int i0 = c * stride + base;
+            float d[V], g[V], b[V];
+            read(i0, d, 0.0f);
+            if (hr != nullptr) store_guarded<V>(hr, i0, cols, d);
+            load_window<V>(a.w, i0, cols, g, 0.0f);
+            load_window<V>(a.beta, i0, cols, b, 0.0f);
+#pragma unroll
+            for (int e = 0; e < V; ++e) d[e] = (d[e] - mean) * rstd * g[e] + b[e];
+            store_guarded<V>(a.y + off, i0, cols, d);
+        }
+    }
+}
+
+// ---- host-side dispatch over the compiled instances -------------------------------
+
+template <int OP, int V, int NCHUNK, int SEG>
+int launch_reg(bool exact, const Args &a, dim3 grid, dim3 block, hipStream_t s) {
+    if (exact) hipLaunchKernelGGL((reg_kernel<OP, V, NCHUNK, SEG, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((reg_kernel<OP, V, NCHUNK, SEG, false>), grid, block, 0, s, a);
+    return (int)hipGetLastError();
+}
+
+template <int OP, int V, int SEG>
+int launch_by_chunks(int chunks, bool exact, const Args &a, dim3 grid, dim3 block, hipStream_t s) {
+    switch (chunks) {
+        case 1: return launch_reg<OP, V, 1, SEG>(exact, a, grid, block, s);
+        case 2: return launch_reg<OP, V, 2, SEG>(exact, a, grid, block, s);
+        case 4: return launch_reg<OP, V, 4, SEG>(exact, a, grid, block, s);
+        case 8: return launch_reg<OP, V, 8, SEG>(exact, a, grid, block, s);
+        default: return (int)hipErrorInvalidValue;
+    }
+}
+
+template <int OP, int SEG>
+int launch_by_v(int v, int chunks, bool exact, const Args &a, dim3 grid, dim3 block, hipStream_t s) {
+    switch (v) {
+        case 1: return launch_by_chunks<OP, 1, SEG>(chunks, exact, a, grid, block, s);
+        case 2: return launch_by_chunks<OP, 2, SEG>(chunks, exact, a, grid, block, s);
+        case 4: return launch_by_chunks<OP, 4, SEG>(chunks, exact, a, grid, block, s);
+        default: return (int)hipErrorInvalidValue;
+    }
+}
+
+// Launch `OP` with a plan already checked by the planner.
+template <int OP>
+int launch_op(const rr_plan &p, const Args &args, void *stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    Args a = args;
+    a.lanes_per_row = p.lanes_per_row;
+    a.log2_lanes = __builtin_ctz((unsigned)p.lanes_per_row);
+    a.rows_per_group = p.rows_per_group;
+    const int64_t groups = (a.rows + p.rows_per_group - 1) / p.rows_per_group;
+    const dim3 grid((unsigned)groups), block((unsigned)p.block);
+    if (p.path == RR_PATH_LOOP) {
+        switch (p.v) {
+            case 1: hipLaunchKernelGGL((loop_kernel<OP, 1>), grid, block, 0, s, a); break;
+            case 2: hipLaunchKernelGGL((loop_kernel<OP, 2>), grid, block, 0, s, a); break;
+            case 4: hipLaunchKernelGGL((loop_kernel<OP, 4>), grid, block, 0, s, a); break;
+            default: return (int)hipErrorInvalidValue;
+        }
+        return (int)hipGetLastError();
+    }
+    const int chunks = p.slots / p.v;
+    const bool exact = (int64_t)p.lanes_per_row * p.slots == (int64_t)a.cols;
+    switch (p.lanes_per_row) {
+        case 8: return launch_by_v<OP, 8>(p.v, chunks, exact, a, grid, block, s);
+        case 16: return launch_by_v<OP, 16>(p.v, chunks, exact, a, grid, block, s);
+        case 32: return launch_by_v<OP, 32>(p.v, chunks, exact, a, grid, block, s);
+        default: return launch_by_v<OP, 64>(p.v, chunks, exact, a, grid, block, s);
+    }
+}
+
+}  // namespace rowred

@@ -1,0 +1,41 @@
+// Shared between the host entry points and the device kernels of librowred.
+#pragma once
+
+#include <stdint.h>
+
+#include "rowred.h"
+
+namespace rowred {
+
+// Everything one launch needs, passed by value as the kernel argument.
+struct Args {
+    const float *x;          // input rows (logits for cross-entropy)
+    const float *residual;   // residual LayerNorm second input, else null
+    const float *w;          // RMSNorm weight / LayerNorm gamma, else null
+    const float *beta;       // LayerNorm beta, else null
+    const int32_t *targets;  // cross-entropy targets, else null
+    float *y;                // per-element output, else null
+    float *h_out;            // residual LayerNorm h = x + residual, may be null
+    float *row_out;          // per-row output (row sum, loss), else null
+    int64_t rows;
+    int32_t cols;
+    int32_t lanes_per_row;   // workers per row (power of two)
+    int32_t log2_lanes;      // log2(lanes_per_row)
+    int32_t rows_per_group;  // rows handled by one workgroup
+    float eps;
+};
+
+// Host-side launchers, one translation unit per operator. Each validates
+// nothing (the entry points do) and returns the HIP status of the launch.
+int launch_rmsnorm(const rr_plan &p, const Args &a, void *stream);
+int launch_row_sum(const rr_plan &p, const Args &a, void *stream);
+int launch_softmax(const rr_plan &p, const Args &a, void *stream);
+int launch_layernorm(const rr_plan &p, const Args &a, void *stream);
+int launch_residual_layernorm(const rr_plan &p, const Args &a, void *stream);
+int launch_cross_entropy(const rr_plan &p, const Args &a, void *stream);
+
+// Planner (plan.cpp; pure host C++).
+int select_plan(int op, int64_t rows, int64_t cols, rr_plan *out);
+int check_plan(int op, int64_t rows, int64_t cols, const rr_plan *plan);
+
+}  // namespace rowred

@@ -1,0 +1,64 @@
+"""Enumeration of legal launch plans for one (op, rows, cols).
+
+The finite search space of the plan selector: which row-to-workgroup family
+(several rows per wavefront, whole wavefronts per row, or the streaming
+loop), how many workers share a row and how many consecutive floats each
+owns per pack. Candidates are generated first and filtered through the
+library's own legality check, so an illegal candidate is never timed
+(LuisaCompute notes, "Consecutive-worker reduction layout checkpoint",
+section "Implementation and semantics": the private-storage bound is enforced
+before any scoring).
+"""
+from __future__ import annotations
+
+from . import _capi
+from ._capi import RR_OK, RR_PATH_LOOP, RR_PATH_PACKED, RR_PATH_ROW, rr_plan
+
+PACKED_LANES = (8, 16, 32)
+PACKED_BLOCKS = (64, 256)
+ROW_LANES = (64, 128, 256, 512, 1024)
+VS = (1, 2, 4)
+CHUNKS = (1, 2, 4, 8)
+LOOP_BLOCKS = (256, 1024)
+
+
+def _min_chunks(cols: int, lanes: int, v: int):
+    for c in CHUNKS:
+        if lanes * v * c >= cols:
+            return c
+    return None
+
+
+def candidate_plans(op: str, rows: int, cols: int, include_loop: bool = True) -> list[rr_plan]:
+    """Every legal plan of the search grid, with the fewest chunks that cover a row."""
+    op_id = _capi.OP_IDS[op]
+    L = _capi.lib()
+    out = []
+
+    def add(p: rr_plan):
+        if L.rr_check_plan(op_id, rows, cols, p) == RR_OK:
+            out.append(p)
+
+    for lanes in PACKED_LANES:
+        for block in PACKED_BLOCKS:
+            for v in VS:
+                c = _min_chunks(cols, lanes, v)
+                if c is not None:
+                    add(rr_plan(RR_PATH_PACKED, block, lanes, block // lanes, v, c * v))
+    for lanes in ROW_LANES:
+        blocks = sorted({lanes, max(lanes, 256)})
+        for block in blocks:
+            for v in VS:
+                c = _min_chunks(cols, lanes, v)
+                if c is not None:
+                    add(rr_plan(RR_PATH_ROW, block, lanes, block // lanes, v, c * v))
+    if include_loop:
+        for block in LOOP_BLOCKS:
+            for v in VS:
+                add(rr_plan(RR_PATH_LOOP, block, block, 1, v, 0))
+    return out
+
+
+def plan_key(p: rr_plan) -> str:
+    name = {RR_PATH_PACKED: "packed", RR_PATH_ROW: "row", RR_PATH_LOOP: "loop"}[p.path]
+    return f"{name}-b{p.block}-w{p.lanes_per_row}-v{p.v}-k{p.slots}"

@@ -1,0 +1,216 @@
+"""C-ABI library: loads, exports what include/rowred.h declares, validates
+arguments and plans on the host (no GPU, no kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from row_reduction_amd import _capi, workloads
+from row_reduction_amd._capi import (RR_ERR_INVALID_ARGUMENT, RR_ERR_UNSUPPORTED, RR_OK,
+                                     RR_PATH_LOOP, RR_PATH_PACKED, RR_PATH_ROW, rr_plan)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rowred.h")
+
+# Non-null, dword-aligned stand-ins: every call below is rejected on the host
+# before any device work, so these are never dereferenced.
+P = ctypes.c_void_p(0x10000)
+MISALIGNED = ctypes.c_void_p(0x10002)
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _capi.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const\s+char\s*\*)\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = declared_functions()
+    assert set(names) == set(_capi.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    assert _capi.status_string(RR_OK) == "RR_OK"
+    assert _capi.status_string(RR_ERR_INVALID_ARGUMENT) == "RR_ERR_INVALID_ARGUMENT"
+    assert _capi.status_string(RR_ERR_UNSUPPORTED) == "RR_ERR_UNSUPPORTED"
+    assert _capi.status_string(3) == "RR_ERR_LAUNCH"
+    assert _capi.status_string(99) == "RR_UNKNOWN_STATUS"
+
+
+# ---------------------------------------------------------------- argument errors
+
+def call(L, op, x=P, rows=4, cols=8, eps=1e-6, plan=None, **kw):
+    """Invoke one entry point with stand-in pointers, overriding some."""
+    if op == "rmsnorm":
+        return L.rmsnorm_f32_ex(x, kw.get("w", P), kw.get("y", P), rows, cols, eps, plan, None)
+    if op == "sum":
+        return L.row_sum_f32_ex(x, kw.get("out", P), rows, cols, plan, None)
+    if op == "softmax":
+        return L.softmax_f32_ex(x, kw.get("y", P), rows, cols, plan, None)
+    if op == "layernorm":
+        return L.layernorm_f32_ex(x, kw.get("gamma", P), kw.get("beta", P), kw.get("y", P), rows,
+                                  cols, eps, plan, None)
+    if op == "residual_layernorm":
+        return L.residual_layernorm_f32_ex(x, kw.get("residual", P), kw.get("gamma", P),
+                                           kw.get("beta", P), kw.get("y", P), kw.get("h", None),
+                                           rows, cols, eps, plan, None)
+    if op == "cross_entropy":
+        return L.cross_entropy_f32_ex(x, kw.get("targets", P), kw.get("loss", P), rows, cols, plan,
+                                      None)
+    raise ValueError(op)
+
+
+OPS = list(_capi.OP_IDS)
+
+
+@pytest.mark.parametrize("op", OPS)
+def test_rows_zero_is_ok_without_launch(L, op):
+    assert call(L, op, rows=0) == RR_OK
+    # Even with null pointers: nothing is touched.
+    assert call(L, op, x=NULL, rows=0) == RR_OK
+
+
+@pytest.mark.parametrize("op", OPS)
+def test_bad_shapes(L, op):
+    assert call(L, op, rows=-1) == RR_ERR_INVALID_ARGUMENT
+    assert call(L, op, cols=0) == RR_ERR_INVALID_ARGUMENT
+    assert call(L, op, cols=-5) == RR_ERR_INVALID_ARGUMENT
+    assert call(L, op, cols=1 << 31) == RR_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("op", OPS)
+def test_null_and_misaligned_pointers(L, op):
+    assert call(L, op, x=NULL) == RR_ERR_INVALID_ARGUMENT
+    assert call(L, op, x=MISALIGNED) == RR_ERR_INVALID_ARGUMENT
+    out_kw = {"rmsnorm": "y", "sum": "out", "softmax": "y", "layernorm": "y",
+              "residual_layernorm": "y", "cross_entropy": "loss"}[op]
+    assert call(L, op, **{out_kw: NULL}) == RR_ERR_INVALID_ARGUMENT
+    assert call(L, op, **{out_kw: MISALIGNED}) == RR_ERR_INVALID_ARGUMENT
+
+
+def test_operator_specific_pointers(L):
+    assert call(L, "rmsnorm", w=NULL) == RR_ERR_INVALID_ARGUMENT
+    assert call(L, "layernorm", gamma=NULL) == RR_ERR_INVALID_ARGUMENT
+    assert call(L, "layernorm", beta=MISALIGNED) == RR_ERR_INVALID_ARGUMENT
+    assert call(L, "residual_layernorm", residual=NULL) == RR_ERR_INVALID_ARGUMENT
+    assert call(L, "residual_layernorm", h=MISALIGNED) == RR_ERR_INVALID_ARGUMENT
+    assert call(L, "cross_entropy", targets=NULL) == RR_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("op", ["rmsnorm", "layernorm", "residual_layernorm"])
+@pytest.mark.parametrize("eps", [-1e-6, float("nan"), float("inf")])
+def test_bad_eps(L, op, eps):
+    assert call(L, op, eps=eps) == RR_ERR_INVALID_ARGUMENT
+
+
+# ---------------------------------------------------------------- plans
+
+def plan(path, block, lanes, v, slots):
+    return rr_plan(path, block, lanes, block // lanes, v, slots)
+
+
+ILLEGAL = [
+    plan(RR_PATH_ROW, 256, 256, 3, 12),        # V = 3
+    plan(RR_PATH_ROW, 256, 96, 4, 16),         # lanes not a power of two
+    plan(RR_PATH_ROW, 2048, 1024, 4, 16),      # block above 1024
+    plan(RR_PATH_ROW, 32, 32, 4, 16),          # block below one wavefront
+    plan(RR_PATH_ROW, 256, 512, 4, 16),        # lanes > block
+    plan(RR_PATH_ROW, 256, 256, 4, 64),        # 16 chunks: over the register budget
+    plan(RR_PATH_ROW, 256, 256, 4, 12),        # 3 chunks: not a power of two
+    plan(RR_PATH_ROW, 256, 64, 4, 4),          # too few slots for 4096 columns
+    plan(RR_PATH_ROW, 256, 32, 4, 32),         # ROW needs >= 64 lanes
+    plan(RR_PATH_PACKED, 256, 64, 4, 16),      # PACKED needs < 64 lanes
+    plan(RR_PATH_LOOP, 256, 128, 4, 0),        # LOOP: one row per group
+    plan(RR_PATH_LOOP, 256, 256, 4, 16),       # LOOP keeps no slots
+    rr_plan(RR_PATH_ROW, 256, 128, 1, 4, 16),  # rows_per_group inconsistent
+    rr_plan(7, 256, 256, 1, 4, 16),            # unknown path
+]
+
+
+@pytest.mark.parametrize("bad", ILLEGAL, ids=lambda p: str(p.as_dict()))
+def test_illegal_plans_fail_closed(L, bad):
+    assert L.rr_check_plan(0, 64, 4096, bad) == RR_ERR_UNSUPPORTED
+    # The entry points refuse them before launching anything.
+    for op in OPS:
+        assert call(L, op, rows=64, cols=4096, plan=bad) == RR_ERR_UNSUPPORTED
+
+
+def test_v_wider_than_row_is_rejected(L):
+    assert L.rr_check_plan(0, 1, 3, plan(RR_PATH_PACKED, 64, 8, 4, 4)) == RR_ERR_UNSUPPORTED
+    assert L.rr_check_plan(0, 1, 3, plan(RR_PATH_PACKED, 64, 8, 2, 2)) == RR_OK
+
+
+def test_check_plan_argument_errors(L):
+    good = plan(RR_PATH_ROW, 256, 256, 4, 16)
+    assert L.rr_check_plan(0, 64, 4096, good) == RR_OK
+    assert L.rr_check_plan(9, 64, 4096, good) == RR_ERR_INVALID_ARGUMENT
+    assert L.rr_check_plan(0, 64, 0, good) == RR_ERR_INVALID_ARGUMENT
+    assert L.rr_check_plan(0, 64, 4096, None) == RR_ERR_INVALID_ARGUMENT
+    assert L.rr_select_plan(9, 1, 1, rr_plan()) == RR_ERR_INVALID_ARGUMENT
+    assert L.rr_select_plan(0, 1, 1, None) == RR_ERR_INVALID_ARGUMENT
+
+
+SHAPES = [(1, 1), (1, 2), (1, 3), (5, 31), (5, 33), (1, 127), (5, 128), (5, 129), (17, 257),
+          (5, 4103), (64, 4096), (1024, 4096), (16384, 8192), (3, 32768), (2, 32769), (2, 100000),
+          (100000, 16), (0, 7)]
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES)
+@pytest.mark.parametrize("op", OPS)
+def test_selected_plans_are_legal_and_cover_the_row(L, op, rows, cols):
+    p = rr_plan()
+    assert L.rr_select_plan(_capi.OP_IDS[op], rows, cols, p) == RR_OK
+    assert L.rr_check_plan(_capi.OP_IDS[op], rows, cols, p) == RR_OK
+    assert p.rows_per_group * p.lanes_per_row == p.block
+    if p.path != RR_PATH_LOOP:
+        # The ownership map's private-slot bound fits the plan's registers.
+        assert oracle.slot_bound(cols, p.lanes_per_row, p.v) <= p.slots
+        assert p.lanes_per_row * p.slots >= cols
+    else:
+        assert cols > 1024 * 32 or p.slots == 0
+
+
+def test_page_packing_arithmetic(L):
+    """17 rows packed eight to a group need three groups (LuisaCompute page,
+    "Result" section, the 17x257 remark)."""
+    p = plan(RR_PATH_PACKED, 256, 32, 4, 16)
+    assert p.rows_per_group == 8
+    assert L.rr_check_plan(0, 17, 257, p) == RR_OK
+    assert -(-17 // p.rows_per_group) == 3
+
+
+def test_page_plans_are_expressible(L):
+    """The page's worker / V choices map onto legal plans here (one row per
+    group) with the slot count the ownership bound gives."""
+    for rows, cols, workers, v in [(1, 127, 32, 4), (17, 257, 256, 4), (64, 4096, 128, 4),
+                                   (1024, 4096, 256, 2)]:
+        need = oracle.slot_bound(cols, workers, v)
+        chunks = 1
+        while chunks * v < need:
+            chunks *= 2
+        path = RR_PATH_PACKED if workers < 64 else RR_PATH_ROW
+        block = max(64, workers)
+        p = plan(path, block, workers, v, chunks * v)
+        assert L.rr_check_plan(0, rows, cols, p) == RR_OK, (rows, cols, workers, v)
+
+
+def test_algorithmic_bytes_table():
+    """Byte counts of one call: each input read once, each output written once."""
+    assert workloads.algorithmic_bytes("rmsnorm", 16384, 8192) == 1073774592
+    assert workloads.algorithmic_bytes("rmsnorm", 1024, 4096) == 33570816
+    assert workloads.algorithmic_bytes("sum", 1024, 4096) == 16781312
+    assert workloads.algorithmic_bytes("residual_layernorm", 64, 4096) == 3178496
+    assert workloads.algorithmic_bytes("cross_entropy", 17, 257) == 17612
