@@ -104,66 +104,61 @@ def batch_us(torch, fn, target_ms: float = 20.0, rounds: int = 3, samples: int =
             "launches_per_sample": n}
 
 
-def shape_table(torch, rr, workloads, device) -> list:
-    """us/op and GB/s for every measured shape and operator."""
-    import numpy as np
+def graph_us(torch, fn, n: int, samples: int = 15) -> dict:
+    """Median us per call over replays of a HIP graph of n calls of fn."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    timer = Timer(torch)
+    g.replay()
+    torch.cuda.synchronize()
+    vals = sorted(timer.time_ms(g.replay, 1) * 1000.0 / n for _ in range(samples))
+    return {"us": vals[len(vals) // 2], "min_us": vals[0], "max_us": vals[-1]}
+
+
+def shape_table(torch, rr, workloads, device, samples: int = 15) -> list:
+    """us/op and GB/s for every measured shape and operator with the selected
+    plan. Each sample replays a HIP graph of back-to-back launches (GPU time
+    per call, host launch cost excluded); working sets of 1 MiB or more are
+    also timed cold, cycling >= 768 MiB of distinct buffers. `single_call_us`
+    is one synchronised host call, launch to completion."""
+    from row_reduction_amd.tune import Case, GraphTimer, launches_per_graph
     out = []
-
-    def record(op, rows, cols, res, cold, plan=None):
-        nbytes = workloads.algorithmic_bytes(op, rows, cols)
-        us = res["us"]
-        gbps = nbytes / (us * 1e3)
-        out.append({"op": op, "shape": f"{rows}x{cols}", "cache": "cold" if cold else "hot",
-                    "us_per_op": round(us, 3), "min_us": round(res["min_us"], 3),
-                    "max_us": round(res["max_us"], 3), "rows_per_s": round(rows / (us * 1e-6), 1),
-                    "GBps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
-                    "plan": plan})
-
-    # RMSNorm configurations 1-4.
-    for k in (1, 2, 3, 4):
-        for wl in workloads.config_workloads(k):
-            if (wl.rows, wl.cols) == HEADLINE:
+    pairs = [("rmsnorm", s) for s in [(1, 127), (17, 257), (64, 4096), (1024, 4096)]]
+    pairs += [(op, s) for s in workloads.FAMILY_SHAPES for op in workloads.OPS if op != "rmsnorm"]
+    for op, (rows, cols) in pairs:
+        plan = rr.rr_select_plan(op, rows, cols)
+        for hot in (True, False):
+            case = Case(torch, op, rows, cols, False, device, hot=hot)
+            if not hot and not case.cold_possible:
                 continue
-            x = torch.from_numpy(wl.x).to(device)
-            w = torch.from_numpy(wl.w).to(device)
-            y = torch.empty_like(x)
-            plan = rr.rr_select_plan("rmsnorm", wl.rows, wl.cols).as_dict()
-            res = batch_us(torch, lambda: rr.rmsnorm_f32(x, w, wl.eps, y=y))
-            record("rmsnorm", wl.rows, wl.cols, res, False, plan)
-            set_bytes = 2 * x.numel() * 4
-            if set_bytes >= (1 << 20) and set_bytes * 8 < COLD_SET_BYTES:
-                nsets = max(2, COLD_SET_BYTES // set_bytes)
-                if nsets <= 1024:
-                    xs = [x.clone() for _ in range(nsets)]
-                    ys = [torch.empty_like(x) for _ in range(nsets)]
-                    it = [0]
-
-                    def cold_call():
-                        i = it[0] = (it[0] + 1) % nsets
-                        rr.rmsnorm_f32(xs[i], w, wl.eps, y=ys[i])
-                    record("rmsnorm", wl.rows, wl.cols, batch_us(torch, cold_call), True, plan)
-                    del xs, ys
-            del x, w, y
-    # Reduction family, configuration 5.
-    for rows, cols in workloads.FAMILY_SHAPES:
-        d = workloads.family_inputs(rows, cols, 1005)
-        t = {k: torch.from_numpy(v).to(device) for k, v in d.items()}
-        y = torch.empty_like(t["x"])
-        loss = torch.empty(rows, dtype=torch.float32, device=device)
-        calls = {
-            "sum": lambda: rr.row_sum_f32(t["x"], out=loss),
-            "softmax": lambda: rr.softmax_f32(t["x"], y=y),
-            "layernorm": lambda: rr.layernorm_f32(t["x"], t["gamma"], t["beta"], 1e-5, y=y),
-            "residual_layernorm": lambda: rr.residual_layernorm_f32(
-                t["x"], t["residual"], t["gamma"], t["beta"], 1e-5, y=y),
-            "cross_entropy": lambda: rr.cross_entropy_f32(t["x"], t["targets"], loss=loss),
-        }
-        for op, fn in calls.items():
-            plan = rr.rr_select_plan(op, rows, cols).as_dict()
-            record(op, rows, cols, batch_us(torch, fn), False, plan)
-        del t, y, loss
-    torch.cuda.empty_cache()
-    _ = np  # numpy kept for symmetry with the generators
+            n = launches_per_graph(torch, case, plan)
+            gt = GraphTimer(torch, case, plan, n)
+            vals = sorted(gt.sample_us() for _ in range(samples))
+            us = vals[len(vals) // 2]
+            single = []
+            if hot:
+                for _ in range(21):
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    case.launch(0, plan)
+                    torch.cuda.synchronize()
+                    single.append((time.perf_counter() - t0) * 1e6)
+                single.sort()
+            nbytes = workloads.algorithmic_bytes(op, rows, cols)
+            gbps = nbytes / (us * 1e3)
+            out.append({"op": op, "shape": f"{rows}x{cols}", "cache": "cold" if case.cold else "hot",
+                        "us_per_op": round(us, 3), "min_us": round(vals[0], 3),
+                        "max_us": round(vals[-1], 3), "launches_per_graph": n,
+                        "rows_per_s": round(rows / (us * 1e-6), 1), "GBps": round(gbps, 1),
+                        "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                        "single_call_us": round(single[len(single) // 2], 2) if single else None,
+                        "plan": plan.as_dict()})
+            del gt, case
+            torch.cuda.empty_cache()
     return out
 
 
@@ -269,7 +264,7 @@ def main() -> int:
     copy_src = x.view(-1)
     copy_dst = y.view(-1)
     copy = batch_us(torch, lambda: rr.rr_copy_f32(copy_src, copy_dst), rounds=1)
-    empty = batch_us(torch, lambda: rr.rr_empty_kernel(), rounds=1)
+    empty = graph_us(torch, lambda: rr.rr_empty_kernel(), 200)
     copy_gbps = 8 * rows * cols / (copy["us"] * 1e3)
 
     y_sample = None

@@ -94,7 +94,12 @@ typedef enum rr_path {
  *   v               consecutive floats per worker pack: 1, 2 or 4
  *   slots           floats each worker keeps in registers: chunks * v with
  *                   chunks in {1, 2, 4, 8}; cols <= lanes_per_row * slots.
- *                   0 on the LOOP path. */
+ *                   0 on the LOOP path.
+ *   cache           cache policy for the row data: 0 = default; 1 = output
+ *                   stores non-temporal; 2 = row loads (x, residual) and
+ *                   output stores non-temporal. Weights (w, gamma, beta) are
+ *                   always loaded with the default policy. Results do not
+ *                   depend on it. */
 typedef struct rr_plan {
     int32_t path;
     int32_t block;
@@ -102,6 +107,7 @@ typedef struct rr_plan {
     int32_t rows_per_group;
     int32_t v;
     int32_t slots;
+    int32_t cache;
 } rr_plan;
 
 /* RMSNorm: y[r,c] = x[r,c] * w[c] / sqrt(mean_c x[r,c]^2 + eps).

@@ -9,7 +9,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "librowred.so")
+# ROWRED_LIB selects another build of the library (e.g. one compiled with
+# different streaming hints); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("ROWRED_LIB") or os.path.join(HERE, "librowred.so")
 
 RR_OK = 0
 RR_ERR_INVALID_ARGUMENT = 1
@@ -55,6 +57,7 @@ class rr_plan(ctypes.Structure):
         ("rows_per_group", ctypes.c_int32),
         ("v", ctypes.c_int32),
         ("slots", ctypes.c_int32),
+        ("cache", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:
@@ -62,7 +65,7 @@ class rr_plan(ctypes.Structure):
 
     @classmethod
     def from_dict(cls, d: dict) -> "rr_plan":
-        return cls(**{name: int(d[name]) for name, _ in cls._fields_})
+        return cls(**{name: int(d.get(name, 0)) for name, _ in cls._fields_})
 
     def __repr__(self) -> str:
         return f"rr_plan({self.as_dict()})"

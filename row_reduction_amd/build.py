@@ -64,18 +64,26 @@ def _run(cmd: list[str]) -> None:
         sys.stderr.write("\n".join(lines) + "\n")
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    """Compile every source and link librowred.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, verbose: bool = False, defines: list[str] | None = None,
+          out: str | None = None) -> str:
+    """Compile every source and link librowred.so (or `out`); returns the library path.
+
+    `defines` are extra -D macros for the device sources (build variants)."""
+    defines = defines or []
+    tag = "_".join(d.replace("=", "") for d in defines)
+    bdir = os.path.join(BUILD, tag) if tag else BUILD
+    os.makedirs(bdir, exist_ok=True)
+    lib = out or LIB
     cc = hipcc()
     cmds = []
     objs = []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([cc, *hip_flags(), "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *hip_flags(), *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
+                     "-o", obj])
     for src in CXX_SOURCES:
-        obj = os.path.join(BUILD, src.replace(".cpp", ".o"))
+        obj = os.path.join(bdir, src.replace(".cpp", ".o"))
         objs.append(obj)
         cmds.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}",
                      "-I/opt/rocm/include", "-c", os.path.join(CSRC, src), "-o", obj])
@@ -83,13 +91,18 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         for fut in [ex.submit(_run, c) for c in cmds]:
             fut.result()
-    tmp = LIB + f".tmp{os.getpid()}"
+    tmp = lib + f".tmp{os.getpid()}"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    import argparse
+    ap = argparse.ArgumentParser(description="build librowred.so for gfx950")
+    ap.add_argument("-D", "--define", action="append", default=[], help="extra device macro")
+    ap.add_argument("-o", "--out", default=None, help="output library path")
+    a = ap.parse_args()
+    build(verbose=True, defines=a.define, out=a.out)

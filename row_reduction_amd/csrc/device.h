@@ -43,17 +43,45 @@ enum OpId { kRmsNorm = 0, kSum = 1, kSoftmax = 2, kLayerNorm = 3, kResidualLayer
 typedef float f32x2u __attribute__((ext_vector_type(2), aligned(4)));
 typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
 
-template <int V>
+// Cache policy of a launch (rr_plan.cache): rows are touched once, so their
+// loads and stores may carry the non-temporal ("nt") hint, which keeps them
+// from displacing useful lines and shortens the end-of-kernel write-back.
+// Weights are shared by every row and must stay cached: their loads never
+// take the hint. HINT bit 0: non-temporal stores; bit 1: non-temporal row
+// loads.
+constexpr int kHintNtStore = 1;
+constexpr int kHintNtLoad = 2;
+constexpr int hint_of_cache(int cache) { return cache == 0 ? 0 : (cache == 1 ? kHintNtStore : kHintNtStore | kHintNtLoad); }
+
+// Overloads on the dword-aligned types (a template over the value type would
+// lose the typedefs' 4-byte alignment and assume natural vector alignment).
+#define ROWRED_LDST(T)                                                                    \
+    template <int HINT, bool STREAM>                                                      \
+    __device__ __forceinline__ T ld(const T *p) {                                         \
+        if constexpr (STREAM && (HINT & kHintNtLoad)) return __builtin_nontemporal_load(p); \
+        else return *p;                                                                   \
+    }                                                                                     \
+    template <int HINT>                                                                   \
+    __device__ __forceinline__ void st(T *p, T v) {                                       \
+        if constexpr (HINT & kHintNtStore) __builtin_nontemporal_store(v, p);              \
+        else *p = v;                                                                      \
+    }
+ROWRED_LDST(float)
+ROWRED_LDST(f32x2u)
+ROWRED_LDST(f32x4u)
+#undef ROWRED_LDST
+
+template <int V, int HINT = 0, bool STREAM = false>
 __device__ __forceinline__ void load_pack(const float *__restrict__ p, float *d) {
     if constexpr (V == 1) {
-        d[0] = p[0];
+        d[0] = ld<HINT, STREAM>(p);
     } else if constexpr (V == 2) {
-        f32x2u t = *reinterpret_cast<const f32x2u *>(p);
+        f32x2u t = ld<HINT, STREAM>(reinterpret_cast<const f32x2u *>(p));
         d[0] = t.x;
         d[1] = t.y;
     } else {
         static_assert(V == 4, "V must be 1, 2 or 4");
-        f32x4u t = *reinterpret_cast<const f32x4u *>(p);
+        f32x4u t = ld<HINT, STREAM>(reinterpret_cast<const f32x4u *>(p));
         d[0] = t.x;
         d[1] = t.y;
         d[2] = t.z;
@@ -61,22 +89,22 @@ __device__ __forceinline__ void load_pack(const float *__restrict__ p, float *d)
     }
 }
 
-template <int V>
+template <int V, int HINT = 0>
 __device__ __forceinline__ void store_pack(float *__restrict__ p, const float *d) {
     if constexpr (V == 1) {
-        p[0] = d[0];
+        st<HINT>(p, d[0]);
     } else if constexpr (V == 2) {
         f32x2u t;
         t.x = d[0];
         t.y = d[1];
-        *reinterpret_cast<f32x2u *>(p) = t;
+        st<HINT>(reinterpret_cast<f32x2u *>(p), t);
     } else {
         f32x4u t;
         t.x = d[0];
         t.y = d[1];
         t.z = d[2];
         t.w = d[3];
-        *reinterpret_cast<f32x4u *>(p) = t;
+        st<HINT>(reinterpret_cast<f32x4u *>(p), t);
     }
 }
 
@@ -85,17 +113,17 @@ __device__ __forceinline__ void store_pack(float *__restrict__ p, const float *d
 // starts at min(i0, cols - V), and each slot then picks its column out of
 // the window, or `fill` when the column lies past the row end. A complete
 // pack reads exactly its own columns; nothing outside the row is read.
-template <int V>
+template <int V, int HINT = 0, bool STREAM = false>
 __device__ __forceinline__ void load_window(const float *__restrict__ row, int i0, int cols, float *d,
                                             float fill) {
     if constexpr (V == 1) {
-        const float t = row[i0 < cols ? i0 : cols - 1];
+        const float t = ld<HINT, STREAM>(row + (i0 < cols ? i0 : cols - 1));
         d[0] = (i0 < cols) ? t : fill;
     } else {
         const int start = i0 < cols - V ? i0 : cols - V;
         const int shift = i0 - start;  // 0 for a complete pack
         float t[V];
-        load_pack<V>(row + start, t);
+        load_pack<V, HINT, STREAM>(row + start, t);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
             const int p = e + shift;
@@ -108,30 +136,30 @@ __device__ __forceinline__ void load_window(const float *__restrict__ row, int i
 }
 
 // Store of the columns of a pack that lie inside the row.
-template <int V>
+template <int V, int HINT = 0>
 __device__ __forceinline__ void store_guarded(float *__restrict__ row, int i0, int cols, const float *d) {
     if (i0 + V <= cols) {
-        store_pack<V>(row + i0, d);
+        store_pack<V, HINT>(row + i0, d);
     } else {
 #pragma unroll
         for (int e = 0; e < V; ++e)
-            if (i0 + e < cols) row[i0 + e] = d[e];
+            if (i0 + e < cols) st<HINT>(row + i0 + e, d[e]);
     }
 }
 
 // Load / store of one pack: plain V-wide access when the row is an exact
 // multiple of the plan's span (every pack complete), else the guarded forms.
-template <int V, bool EXACT>
+template <int V, bool EXACT, int HINT = 0, bool STREAM = false>
 __device__ __forceinline__ void load_slots(const float *__restrict__ row, int i0, int cols, float *d,
                                            float fill) {
-    if constexpr (EXACT) load_pack<V>(row + i0, d);
-    else load_window<V>(row, i0, cols, d, fill);
+    if constexpr (EXACT) load_pack<V, HINT, STREAM>(row + i0, d);
+    else load_window<V, HINT, STREAM>(row, i0, cols, d, fill);
 }
 
-template <int V, bool EXACT>
+template <int V, bool EXACT, int HINT = 0>
 __device__ __forceinline__ void store_slots(float *__restrict__ row, int i0, int cols, const float *d) {
-    if constexpr (EXACT) store_pack<V>(row + i0, d);
-    else store_guarded<V>(row, i0, cols, d);
+    if constexpr (EXACT) store_pack<V, HINT>(row + i0, d);
+    else store_guarded<V, HINT>(row, i0, cols, d);
 }
 
 // ---- combine operations ------------------------------------------------------
@@ -272,8 +300,9 @@ __device__ __forceinline__ T row_reduce(T v, Op op, const RowLanes<SEG> &rl, T *
 // OP: operator; V: floats per pack; NCHUNK: packs per worker (K = V*NCHUNK
 // live floats); SEG: lanes per row when < 64 (several rows per wavefront), or
 // 64 when a row takes lanes_per_row / 64 whole wavefronts; EXACT: the row
-// length equals lanes_per_row * K, so every pack is complete.
-template <int OP, int V, int NCHUNK, int SEG, bool EXACT>
+// length equals lanes_per_row * K, so every pack is complete; HINT: cache
+// policy bits (see hint_of_cache).
+template <int OP, int V, int NCHUNK, int SEG, bool EXACT, int HINT>
 __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
     constexpr int K = V * NCHUNK;
     constexpr bool kMaxFirst = (OP == kSoftmax || OP == kCrossEntropy);
@@ -303,17 +332,18 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
     // ---- load: the worker's K floats stay in registers until the store.
     float v[K];
 #pragma unroll
-    for (int c = 0; c < NCHUNK; ++c) load_slots<V, EXACT>(a.x + off, c * stride + base, cols, &v[c * V], fill);
+    for (int c = 0; c < NCHUNK; ++c)
+        load_slots<V, EXACT, HINT, true>(a.x + off, c * stride + base, cols, &v[c * V], fill);
     if constexpr (OP == kResidualLayerNorm) {
         float r[K];
 #pragma unroll
         for (int c = 0; c < NCHUNK; ++c)
-            load_slots<V, EXACT>(a.residual + off, c * stride + base, cols, &r[c * V], 0.0f);
+            load_slots<V, EXACT, HINT, true>(a.residual + off, c * stride + base, cols, &r[c * V], 0.0f);
 #pragma unroll
         for (int k = 0; k < K; ++k) v[k] = v[k] + r[k];
         if (a.h_out != nullptr && row_ok) {
 #pragma unroll
-            for (int c = 0; c < NCHUNK; ++c) store_slots<V, EXACT>(a.h_out + off, c * stride + base, cols, &v[c * V]);
+            for (int c = 0; c < NCHUNK; ++c) store_slots<V, EXACT, HINT>(a.h_out + off, c * stride + base, cols, &v[c * V]);
         }
     }
 
@@ -334,7 +364,7 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
                 float o[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e) o[e] = v[c * V + e] * inv * wv[c * V + e];
-                store_slots<V, EXACT>(a.y + off, c * stride + base, cols, o);
+                store_slots<V, EXACT, HINT>(a.y + off, c * stride + base, cols, o);
             }
         }
     } else if constexpr (OP == kSum) {
@@ -362,7 +392,7 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
                     float o[V];
 #pragma unroll
                     for (int e = 0; e < V; ++e) o[e] = v[c * V + e] * rz;
-                    store_slots<V, EXACT>(a.y + off, c * stride + base, cols, o);
+                    store_slots<V, EXACT, HINT>(a.y + off, c * stride + base, cols, o);
                 }
             }
         } else {
@@ -400,7 +430,7 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
                 float o[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e) o[e] = v[c * V + e] * rstd * g[c * V + e] + b[c * V + e];
-                store_slots<V, EXACT>(a.y + off, c * stride + base, cols, o);
+                store_slots<V, EXACT, HINT>(a.y + off, c * stride + base, cols, o);
             }
         }
     }
@@ -411,7 +441,7 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
 // One row per workgroup, W = blockDim.x workers, the same ownership map with as
 // many chunks as the row needs. Every pass re-reads the row from memory, one
 // branch-free window load per pack.
-template <int OP, int V>
+template <int OP, int V, int HINT>
 __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
     __shared__ float lds0[16];
     __shared__ float lds1[16];
@@ -427,10 +457,10 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
 
     // Pack of the row's values (x, or x + residual for residual LayerNorm).
     auto read = [&](int i0, float *d, float fill) {
-        load_window<V>(xr, i0, cols, d, fill);
+        load_window<V, HINT, true>(xr, i0, cols, d, fill);
         if constexpr (OP == kResidualLayerNorm) {
             float r[V];
-            load_window<V>(a.residual + off, i0, cols, r, 0.0f);
+            load_window<V, HINT, true>(a.residual + off, i0, cols, r, 0.0f);
 #pragma unroll
             for (int e = 0; e < V; ++e) d[e] = d[e] + r[e];
         }
@@ -454,7 +484,7 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
             load_window<V>(a.w, i0, cols, wv, 0.0f);
 #pragma unroll
             for (int e = 0; e < V; ++e) d[e] = d[e] * inv * wv[e];
-            store_guarded<V>(a.y + off, i0, cols, d);
+            store_guarded<V, HINT>(a.y + off, i0, cols, d);
         }
     } else if constexpr (OP == kSum) {
         double acc = 0.0;
@@ -493,7 +523,7 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
                 read(i0, d, -INFINITY);
 #pragma unroll
                 for (int e = 0; e < V; ++e) d[e] = expf(d[e] - m) * rz;
-                store_guarded<V>(a.y + off, i0, cols, d);
+                store_guarded<V, HINT>(a.y + off, i0, cols, d);
             }
         } else {
             if (rl.lane == 0) {
@@ -530,72 +560,102 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
             const int i0 = c * stride + base;
             float d[V], g[V], b[V];
             read(i0, d, 0.0f);
-            if (hr != nullptr) store_guarded<V>(hr, i0, cols, d);
+            if (hr != nullptr) store_guarded<V, HINT>(hr, i0, cols, d);
             load_window<V>(a.w, i0, cols, g, 0.0f);
             load_window<V>(a.beta, i0, cols, b, 0.0f);
 #pragma unroll
             for (int e = 0; e < V; ++e) d[e] = (d[e] - mean) * rstd * g[e] + b[e];
-            store_guarded<V>(a.y + off, i0, cols, d);
+            store_guarded<V, HINT>(a.y + off, i0, cols, d);
         }
     }
 }
 
 // ---- host-side dispatch over the compiled instances -------------------------------
 
-template <int OP, int V, int NCHUNK, int SEG>
-int launch_reg(bool exact, const Args &a, dim3 grid, dim3 block, hipStream_t s) {
-    if (exact) hipLaunchKernelGGL((reg_kernel<OP, V, NCHUNK, SEG, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((reg_kernel<OP, V, NCHUNK, SEG, false>), grid, block, 0, s, a);
+struct Launch {
+    dim3 grid, block;
+    hipStream_t stream;
+    bool exact;
+    int cache;
+};
+
+template <int OP, int V, int NCHUNK, int SEG, bool EXACT>
+int launch_reg_exact(const Args &a, const Launch &l) {
+    switch (l.cache) {
+        case 0: hipLaunchKernelGGL((reg_kernel<OP, V, NCHUNK, SEG, EXACT, hint_of_cache(0)>), l.grid, l.block, 0, l.stream, a); break;
+        case 1: hipLaunchKernelGGL((reg_kernel<OP, V, NCHUNK, SEG, EXACT, hint_of_cache(1)>), l.grid, l.block, 0, l.stream, a); break;
+        case 2: hipLaunchKernelGGL((reg_kernel<OP, V, NCHUNK, SEG, EXACT, hint_of_cache(2)>), l.grid, l.block, 0, l.stream, a); break;
+        default: return (int)hipErrorInvalidValue;
+    }
     return (int)hipGetLastError();
 }
 
+template <int OP, int V, int NCHUNK, int SEG>
+int launch_reg(const Args &a, const Launch &l) {
+    return l.exact ? launch_reg_exact<OP, V, NCHUNK, SEG, true>(a, l)
+                   : launch_reg_exact<OP, V, NCHUNK, SEG, false>(a, l);
+}
+
 template <int OP, int V, int SEG>
-int launch_by_chunks(int chunks, bool exact, const Args &a, dim3 grid, dim3 block, hipStream_t s) {
+int launch_by_chunks(int chunks, const Args &a, const Launch &l) {
     switch (chunks) {
-        case 1: return launch_reg<OP, V, 1, SEG>(exact, a, grid, block, s);
-        case 2: return launch_reg<OP, V, 2, SEG>(exact, a, grid, block, s);
-        case 4: return launch_reg<OP, V, 4, SEG>(exact, a, grid, block, s);
-        case 8: return launch_reg<OP, V, 8, SEG>(exact, a, grid, block, s);
+        case 1: return launch_reg<OP, V, 1, SEG>(a, l);
+        case 2: return launch_reg<OP, V, 2, SEG>(a, l);
+        case 4: return launch_reg<OP, V, 4, SEG>(a, l);
+        case 8: return launch_reg<OP, V, 8, SEG>(a, l);
         default: return (int)hipErrorInvalidValue;
     }
 }
 
 template <int OP, int SEG>
-int launch_by_v(int v, int chunks, bool exact, const Args &a, dim3 grid, dim3 block, hipStream_t s) {
+int launch_by_v(int v, int chunks, const Args &a, const Launch &l) {
     switch (v) {
-        case 1: return launch_by_chunks<OP, 1, SEG>(chunks, exact, a, grid, block, s);
-        case 2: return launch_by_chunks<OP, 2, SEG>(chunks, exact, a, grid, block, s);
-        case 4: return launch_by_chunks<OP, 4, SEG>(chunks, exact, a, grid, block, s);
+        case 1: return launch_by_chunks<OP, 1, SEG>(chunks, a, l);
+        case 2: return launch_by_chunks<OP, 2, SEG>(chunks, a, l);
+        case 4: return launch_by_chunks<OP, 4, SEG>(chunks, a, l);
         default: return (int)hipErrorInvalidValue;
     }
+}
+
+template <int OP, int V>
+int launch_loop(const Args &a, const Launch &l) {
+    switch (l.cache) {
+        case 0: hipLaunchKernelGGL((loop_kernel<OP, V, hint_of_cache(0)>), l.grid, l.block, 0, l.stream, a); break;
+        case 1: hipLaunchKernelGGL((loop_kernel<OP, V, hint_of_cache(1)>), l.grid, l.block, 0, l.stream, a); break;
+        case 2: hipLaunchKernelGGL((loop_kernel<OP, V, hint_of_cache(2)>), l.grid, l.block, 0, l.stream, a); break;
+        default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
 }
 
 // Launch `OP` with a plan already checked by the planner.
 template <int OP>
 int launch_op(const rr_plan &p, const Args &args, void *stream) {
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     Args a = args;
     a.lanes_per_row = p.lanes_per_row;
     a.log2_lanes = __builtin_ctz((unsigned)p.lanes_per_row);
     a.rows_per_group = p.rows_per_group;
     const int64_t groups = (a.rows + p.rows_per_group - 1) / p.rows_per_group;
-    const dim3 grid((unsigned)groups), block((unsigned)p.block);
+    Launch l;
+    l.grid = dim3((unsigned)groups);
+    l.block = dim3((unsigned)p.block);
+    l.stream = reinterpret_cast<hipStream_t>(stream);
+    l.exact = (int64_t)p.lanes_per_row * p.slots == (int64_t)a.cols;
+    l.cache = p.cache;
     if (p.path == RR_PATH_LOOP) {
         switch (p.v) {
-            case 1: hipLaunchKernelGGL((loop_kernel<OP, 1>), grid, block, 0, s, a); break;
-            case 2: hipLaunchKernelGGL((loop_kernel<OP, 2>), grid, block, 0, s, a); break;
-            case 4: hipLaunchKernelGGL((loop_kernel<OP, 4>), grid, block, 0, s, a); break;
+            case 1: return launch_loop<OP, 1>(a, l);
+            case 2: return launch_loop<OP, 2>(a, l);
+            case 4: return launch_loop<OP, 4>(a, l);
             default: return (int)hipErrorInvalidValue;
         }
-        return (int)hipGetLastError();
     }
     const int chunks = p.slots / p.v;
-    const bool exact = (int64_t)p.lanes_per_row * p.slots == (int64_t)a.cols;
     switch (p.lanes_per_row) {
-        case 8: return launch_by_v<OP, 8>(p.v, chunks, exact, a, grid, block, s);
-        case 16: return launch_by_v<OP, 16>(p.v, chunks, exact, a, grid, block, s);
-        case 32: return launch_by_v<OP, 32>(p.v, chunks, exact, a, grid, block, s);
-        default: return launch_by_v<OP, 64>(p.v, chunks, exact, a, grid, block, s);
+        case 8: return launch_by_v<OP, 8>(p.v, chunks, a, l);
+        case 16: return launch_by_v<OP, 16>(p.v, chunks, a, l);
+        case 32: return launch_by_v<OP, 32>(p.v, chunks, a, l);
+        default: return launch_by_v<OP, 64>(p.v, chunks, a, l);
     }
 }
 

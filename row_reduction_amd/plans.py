@@ -20,6 +20,7 @@ ROW_LANES = (64, 128, 256, 512, 1024)
 VS = (1, 2, 4)
 CHUNKS = (1, 2, 4, 8)
 LOOP_BLOCKS = (256, 1024)
+CACHES = (0, 1, 2)
 
 
 def _min_chunks(cols: int, lanes: int, v: int):
@@ -29,15 +30,19 @@ def _min_chunks(cols: int, lanes: int, v: int):
     return None
 
 
-def candidate_plans(op: str, rows: int, cols: int, include_loop: bool = True) -> list[rr_plan]:
-    """Every legal plan of the search grid, with the fewest chunks that cover a row."""
+def candidate_plans(op: str, rows: int, cols: int, include_loop: bool = True,
+                    caches=(0,)) -> list[rr_plan]:
+    """Every legal plan of the search grid, with the fewest chunks that cover a
+    row, for each cache policy in `caches`."""
     op_id = _capi.OP_IDS[op]
     L = _capi.lib()
     out = []
 
     def add(p: rr_plan):
-        if L.rr_check_plan(op_id, rows, cols, p) == RR_OK:
-            out.append(p)
+        for cache in caches:
+            q = rr_plan.from_dict({**p.as_dict(), "cache": cache})
+            if L.rr_check_plan(op_id, rows, cols, q) == RR_OK:
+                out.append(q)
 
     for lanes in PACKED_LANES:
         for block in PACKED_BLOCKS:
@@ -61,4 +66,4 @@ def candidate_plans(op: str, rows: int, cols: int, include_loop: bool = True) ->
 
 def plan_key(p: rr_plan) -> str:
     name = {RR_PATH_PACKED: "packed", RR_PATH_ROW: "row", RR_PATH_LOOP: "loop"}[p.path]
-    return f"{name}-b{p.block}-w{p.lanes_per_row}-v{p.v}-k{p.slots}"
+    return f"{name}-b{p.block}-w{p.lanes_per_row}-v{p.v}-k{p.slots}-c{p.cache}"

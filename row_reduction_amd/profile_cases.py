@@ -1,0 +1,235 @@
+"""Kernel-duration profile of every measured (operator, shape) under rocprofv3.
+
+`run` launches each case with the plan the library selects — warm-up launches
+first, then `--launches` measured ones back to back from one HIP graph, cache-hot (one buffer set) and, for
+working sets of 1 MiB or more, cache-cold (cycling >= 768 MiB of distinct
+buffers) — plus the library's same-bytes streaming copy and empty kernel, and
+writes a manifest of what it launched, in order. Run it under
+
+  rocprofv3 --kernel-trace --output-format csv -d OUT -o cases -- \\
+      python3 <repo>/row_reduction_amd/profile_cases.py run --manifest OUT/manifest.json
+
+`summarize` then walks the trace's dispatches of librowred kernels in
+dispatch order, attributes them to the manifest's cases (checking each
+dispatch's grid size against the case's), and prints a markdown table of
+kernel durations with algorithmic GB/s and the fraction of the 8 TB/s HBM
+peak:
+
+  python3 <repo>/row_reduction_amd/profile_cases.py summarize OUT/manifest.json OUT/cases_kernel_trace.csv
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import os
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0
+
+
+def cases_list(shapes_only=None):
+    from row_reduction_amd import workloads
+    cases = [("rmsnorm", s) for s in [(1, 127), (17, 257), (64, 4096), (1024, 4096), (16384, 8192)]]
+    cases += [(op, s) for s in workloads.FAMILY_SHAPES for op in workloads.OPS if op != "rmsnorm"]
+    if shapes_only:
+        cases = [c for c in cases if f"{c[1][0]}x{c[1][1]}" in shapes_only]
+    return cases
+
+
+def run(args) -> int:
+    import torch
+
+    import row_reduction_amd as rr
+    from row_reduction_amd import workloads
+    from row_reduction_amd.tune import Case
+
+    rr._capi.lib()
+    device = torch.device("cuda:0")
+    manifest = {"launches": args.launches, "warmup": args.warmup, "entries": []}
+
+    def add(name, kind, count, grid, nbytes, warm, extra=None):
+        e = {"name": name, "kind": kind, "count": count, "grid_size": grid, "bytes": nbytes,
+             "warmup": warm}
+        if extra:
+            e.update(extra)
+        manifest["entries"].append(e)
+
+    for op, (rows, cols) in cases_list(args.shapes):
+        plan = rr.rr_select_plan(op, rows, cols)
+        groups = -(-rows // plan.rows_per_group)
+        grid = groups * plan.block
+        nbytes = workloads.algorithmic_bytes(op, rows, cols)
+        inherently_cold = False
+        for hot in (True, False):
+            if not hot and inherently_cold:
+                break
+            case = Case(torch, op, rows, cols, False, device, hot=hot)
+            if not hot and not case.cold_possible:
+                continue
+            inherently_cold = hot and case.cold
+            label = f"{op} {rows}x{cols} {'cold' if case.cold else 'hot'}"
+            print(f"case {label} plan {plan.as_dict()}", flush=True)
+            # Measured launches run back to back from a HIP graph: a kernel
+            # dispatched onto an idle GPU reports a longer duration.
+            n_warm = max(args.warmup, case.nsets)
+            for i in range(n_warm):
+                case.launch(i, plan)
+            add(label, "op", n_warm, grid, nbytes, True)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(args.launches):
+                    case.launch(n_warm + i, plan)
+            graph.replay()
+            add(label, "op", args.launches, grid, nbytes, False, {"plan": plan.as_dict()})
+            torch.cuda.synchronize()
+            del graph
+            del case
+            torch.cuda.empty_cache()
+
+    # Same-bytes streaming copy (1 GiB moved) and the empty kernel.
+    n = 16384 * 8192
+    src = torch.zeros(n, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    copy_grid = -(-(n // 4) // (256 * 4)) * 256
+    for name, kind, fn, grid, nbytes in (
+            ("rr_copy_f32 2^27 floats", "copy", lambda: rr.rr_copy_f32(src, dst), copy_grid, 8 * n),
+            ("rr_empty_kernel", "empty", lambda: rr.rr_empty_kernel(), 64, 0)):
+        for _ in range(args.warmup):
+            fn()
+        add(name, kind, args.warmup, grid, nbytes, True)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.launches):
+                fn()
+        graph.replay()
+        add(name, kind, args.launches, grid, nbytes, False)
+        torch.cuda.synchronize()
+        del graph
+    os.makedirs(os.path.dirname(os.path.abspath(args.manifest)), exist_ok=True)
+    with open(args.manifest, "w") as f:
+        json.dump(manifest, f)
+    print(f"wrote {args.manifest}", flush=True)
+    return 0
+
+
+def ours(name: str) -> bool:
+    return "rowred::" in name or "copy_kernel" in name or "empty_kernel" in name
+
+
+def summarize(args) -> int:
+    man = json.load(open(args.manifest))
+    rows = [r for r in csv.DictReader(open(args.trace)) if ours(r["Kernel_Name"])]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    pos = 0
+    out = []
+    for e in man["entries"]:
+        chunk = rows[pos:pos + e["count"]]
+        pos += e["count"]
+        if len(chunk) != e["count"]:
+            raise SystemExit(f"trace ended early at {e['name']}")
+        for r in chunk:
+            if int(r.get("Grid_Size") or r["Grid_Size_X"]) != e["grid_size"]:
+                raise SystemExit(f"dispatch {r['Dispatch_Id']} grid {r.get('Grid_Size') or r['Grid_Size_X']} does not match "
+                                 f"{e['name']} ({e['grid_size']})")
+        if e["warmup"]:
+            continue
+        durs = sorted(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in chunk)
+        med = statistics.median(durs)
+        avg = sum(durs) / len(durs)
+        gbps = e["bytes"] / med if e["bytes"] else None
+        out.append((e, chunk[0]["Kernel_Name"], len(durs), avg, med, durs[0], durs[-1], gbps))
+    if pos != len(rows):
+        raise SystemExit(f"{len(rows) - pos} librowred dispatches left unattributed")
+    print("| Case | Kernel | Launches | Avg ns | Median ns | Min ns | Max ns | GB/s (median) | % of 8 TB/s |")
+    print("|---|---|---:|---:|---:|---:|---:|---:|---:|")
+    for e, kname, n, avg, med, lo, hi, gbps in out:
+        k = kname.replace("rowred::", "").replace("(rowred::Args)", "").replace("void ", "")
+        k = k.replace("(anonymous namespace)::", "")
+        g = f"{gbps:.1f}" if gbps else "—"
+        f = f"{100 * gbps / PEAK_GBPS:.1f}" if gbps else "—"
+        print(f"| {e['name']} | `{k}` | {n} | {avg:.0f} | {med:.0f} | {lo} | {hi} | {g} | {f} |")
+    return 0
+
+
+def counters(args) -> int:
+    """Calibrated HBM traffic per launch of the headline RMSNorm kernel from two
+    rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of
+    `bench.py --no-shapes --no-cpu`, which also launches rr_copy_f32 over the
+    same 2^27 floats: each counter is scaled by (bytes the copy must move) /
+    (what the counter reads for the copy)."""
+    import hashlib
+
+    def load(path, counter):
+        per = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return per
+
+    fetch = load(args.fetch_csv, "FETCH_SIZE")
+    write = load(args.write_csv, "WRITE_SIZE")
+    n = 16384 * 8192
+    copy_name = [k for k in fetch if "copy_kernel" in k][0]
+    rms_name = [k for k in fetch if k.startswith("void rowred::reg_kernel<0,")][0]
+    avg = lambda v: sum(v) / len(v)
+    f_copy, w_copy = avg(fetch[copy_name]) * 1024, avg(write[copy_name]) * 1024
+    f_scale, w_scale = 4 * n / f_copy, 4 * n / w_copy
+    f_rms, w_rms = avg(fetch[rms_name]) * 1024 * f_scale, avg(write[rms_name]) * 1024 * w_scale
+    algorithmic = 8 * n + 4 * 8192
+    h = hashlib.sha256()
+    csrc = os.path.join(HERE, "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".h", ".hip", ".cpp", ".inc")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    print(f"Kernel: `{rms_name}` (rmsnorm_f32 16384x8192, plan from the measured table)")
+    print()
+    print("| Counter | Copy kernel raw (KiB/dispatch) | Copy bytes known | Scale | RMSNorm raw (KiB/dispatch) | RMSNorm calibrated bytes |")
+    print("|---|---:|---:|---:|---:|---:|")
+    print(f"| FETCH_SIZE | {f_copy / 1024:.1f} | {4 * n} | {f_scale:.4f} | {avg(fetch[rms_name]):.1f} | {f_rms:.0f} |")
+    print(f"| WRITE_SIZE | {w_copy / 1024:.1f} | {4 * n} | {w_scale:.4f} | {avg(write[rms_name]):.1f} | {w_rms:.0f} |")
+    print()
+    print(f"Algorithmic bytes per launch: {algorithmic}; calibrated traffic / algorithmic = "
+          f"{(f_rms + w_rms) / algorithmic:.4f}.")
+    print()
+    print(f"source_sha256: {h.hexdigest()}")
+    print(f"traffic_bytes_per_launch: {f_rms + w_rms:.0f}")
+    return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--manifest", required=True)
+    r.add_argument("--launches", type=int, default=50)
+    r.add_argument("--warmup", type=int, default=5)
+    r.add_argument("--shapes", default=None, help="comma-separated subset, e.g. 1024x4096")
+    s = sub.add_parser("summarize")
+    s.add_argument("manifest")
+    s.add_argument("trace")
+    c = sub.add_parser("counters")
+    c.add_argument("fetch_csv")
+    c.add_argument("write_csv")
+    args = ap.parse_args()
+    if args.cmd == "counters":
+        return counters(args)
+    if args.cmd == "run":
+        if args.shapes:
+            args.shapes = set(args.shapes.split(","))
+        return run(args)
+    return summarize(args)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

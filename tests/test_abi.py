@@ -137,6 +137,8 @@ ILLEGAL = [
     plan(RR_PATH_LOOP, 256, 256, 4, 16),       # LOOP keeps no slots
     rr_plan(RR_PATH_ROW, 256, 128, 1, 4, 16),  # rows_per_group inconsistent
     rr_plan(7, 256, 256, 1, 4, 16),            # unknown path
+    rr_plan(RR_PATH_ROW, 256, 256, 1, 4, 16, 3),   # unknown cache policy
+    rr_plan(RR_PATH_ROW, 256, 256, 1, 4, 16, -1),  # unknown cache policy
 ]
 
 
@@ -156,6 +158,9 @@ def test_v_wider_than_row_is_rejected(L):
 def test_check_plan_argument_errors(L):
     good = plan(RR_PATH_ROW, 256, 256, 4, 16)
     assert L.rr_check_plan(0, 64, 4096, good) == RR_OK
+    for cache in (0, 1, 2):
+        good.cache = cache
+        assert L.rr_check_plan(0, 64, 4096, good) == RR_OK
     assert L.rr_check_plan(9, 64, 4096, good) == RR_ERR_INVALID_ARGUMENT
     assert L.rr_check_plan(0, 64, 0, good) == RR_ERR_INVALID_ARGUMENT
     assert L.rr_check_plan(0, 64, 4096, None) == RR_ERR_INVALID_ARGUMENT

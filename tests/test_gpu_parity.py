@@ -63,6 +63,31 @@ def test_every_legal_plan_on_ragged_matrix(gpu_device, op, cols):
 
 
 @pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("cols", [129, 4096, 33000])
+def test_cache_policies_give_identical_results(gpu_device, op, cols):
+    """Non-temporal hints change where data is cached, never the arithmetic:
+    every cache policy of a plan must reproduce the default bit for bit."""
+    import torch
+    rows = 5
+    a = family_host_inputs(op, rows, cols, seed=31)
+    ref = run_oracle(op, a)
+    d = to_dev(a, gpu_device)
+    base = [p for p in plans.candidate_plans(op, rows, cols) if p.v == 4 or p.path == 2]
+    for p in base[::3]:
+        outs = []
+        for cache in (0, 1, 2):
+            q = rr.rr_plan.from_dict({**p.as_dict(), "cache": cache})
+            what = f"{op} {rows}x{cols} {plans.plan_key(q)}"
+            announce(what)
+            got = run_gpu(op, d, plan=q, with_h=True)
+            compare(op, got, ref, what)
+            outs.append({k: v.clone() for k, v in got.items()})
+        for o in outs[1:]:
+            for k in o:
+                assert torch.equal(o[k].view(torch.int32), outs[0][k].view(torch.int32)), (op, k)
+
+
+@pytest.mark.parametrize("op", OPS)
 def test_many_packed_rows_and_partial_last_group(gpu_device, op):
     rows, cols = 1003, 24          # 1003 rows: the last group is partly empty
     a = family_host_inputs(op, rows, cols, seed=5)
