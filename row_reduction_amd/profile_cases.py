@@ -186,10 +186,12 @@ def counters(args) -> int:
     f_scale, w_scale = 4 * n / f_copy, 4 * n / w_copy
     f_rms, w_rms = avg(fetch[rms_name]) * 1024 * f_scale, avg(write[rms_name]) * 1024 * w_scale
     algorithmic = 8 * n + 4 * 8192
+    # Same scope as bench.py's kernel_source_hash: the sources that decide
+    # which RMSNorm kernel runs and its code.
     h = hashlib.sha256()
     csrc = os.path.join(HERE, "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".h", ".hip", ".cpp", ".inc")):
+        if name in ("device.h", "internal.h", "kernels_rmsnorm.hip", "plan.cpp", "plan_table.inc"):
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     print(f"Kernel: `{rms_name}` (rmsnorm_f32 16384x8192, plan from the measured table)")
