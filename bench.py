@@ -128,9 +128,32 @@ def shape_table(torch, rr, workloads, device, samples: int = 15) -> list:
     plan. Each sample replays a HIP graph of back-to-back launches (GPU time
     per call, host launch cost excluded); working sets of 1 MiB or more are
     also timed cold, cycling >= 768 MiB of distinct buffers. `single_call_us`
-    is one synchronised host call, launch to completion."""
-    from row_reduction_amd.tune import Case, GraphTimer, launches_per_graph
+    is one synchronised host call, launch to completion. `copy_same_shape_*`
+    is rr_copy_f32 over a matrix of the same shape (8RC bytes) timed the same
+    way: the practical per-call bound at that size."""
+    from row_reduction_amd.tune import COLD_BYTES, Case, GraphTimer, launches_per_graph
     out = []
+    copy_cache = {}
+
+    def copy_ceiling(rows, cols, cold):
+        """Per-call us of rr_copy_f32 moving a rows x cols matrix (8RC bytes),
+        hot or cycling distinct buffers like the cold cases."""
+        key = (rows, cols, cold)
+        if key not in copy_cache:
+            n = rows * cols
+            nsets = max(2, min(1024, COLD_BYTES // (8 * n))) if cold else 1
+            src = [torch.randn(n, device=device) for _ in range(nsets)]
+            dst = [torch.empty(n, device=device) for _ in range(nsets)]
+            it = [0]
+
+            def call():
+                i = it[0] = (it[0] + 1) % nsets
+                rr.rr_copy_f32(src[i], dst[i])
+            reps = max(nsets, 40 if n < (1 << 20) else 8)
+            res = graph_us(torch, call, reps)
+            copy_cache[key] = res["us"]
+            del src, dst
+        return copy_cache[key]
     pairs = [("rmsnorm", s) for s in [(1, 127), (17, 257), (64, 4096), (1024, 4096)]]
     pairs += [(op, s) for s in workloads.FAMILY_SHAPES for op in workloads.OPS if op != "rmsnorm"]
     for op, (rows, cols) in pairs:
@@ -154,12 +177,15 @@ def shape_table(torch, rr, workloads, device, samples: int = 15) -> list:
                 single.sort()
             nbytes = workloads.algorithmic_bytes(op, rows, cols)
             gbps = nbytes / (us * 1e3)
+            cus = copy_ceiling(rows, cols, case.cold)
             out.append({"op": op, "shape": f"{rows}x{cols}", "cache": "cold" if case.cold else "hot",
                         "us_per_op": round(us, 3), "min_us": round(vals[0], 3),
                         "max_us": round(vals[-1], 3), "launches_per_graph": n,
                         "rows_per_s": round(rows / (us * 1e-6), 1), "GBps": round(gbps, 1),
                         "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
                         "single_call_us": round(single[len(single) // 2], 2) if single else None,
+                        "copy_same_shape_us": round(cus, 3),
+                        "copy_same_shape_GBps": round(8 * rows * cols / (cus * 1e3), 1),
                         "plan": plan.as_dict()})
             del gt, case
             torch.cuda.empty_cache()
