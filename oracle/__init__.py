@@ -23,6 +23,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)
 _i32p = ctypes.POINTER(ctypes.c_int32)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
 _i64p = ctypes.POINTER(ctypes.c_int64)
 _i64 = ctypes.c_int64
 
@@ -50,11 +51,19 @@ def _load():
         lib.oracle_rmsnorm_f32.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, ctypes.c_float]
         lib.oracle_row_sum_f32.argtypes = [_f32p, _f32p, _i64, _i64]
         lib.oracle_softmax_f32.argtypes = [_f32p, _f32p, _i64, _i64]
-        lib.oracle_layernorm_f32.argtypes = [_f32p, _f32p, _f32p, _f32p, _i64, _i64,
-                                             ctypes.c_float, _f64p]
+        lib.oracle_layernorm_f32.argtypes = [_f32p, _f32p, _f32p, _f32p, _i64, _i64, ctypes.c_float]
         lib.oracle_residual_layernorm_f32.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
-                                                      _i64, _i64, ctypes.c_float, _f64p]
+                                                      _i64, _i64, ctypes.c_float]
         lib.oracle_cross_entropy_f32.argtypes = [_f32p, _i32p, _f32p, _i64, _i64]
+        lib.oracle_rmsnorm_bf16.argtypes = [_u16p, _u16p, _u16p, _i64, _i64, ctypes.c_float]
+        lib.oracle_row_sum_bf16.argtypes = [_u16p, _f32p, _i64, _i64]
+        lib.oracle_softmax_bf16.argtypes = [_u16p, _u16p, _i64, _i64]
+        lib.oracle_layernorm_bf16.argtypes = [_u16p, _u16p, _u16p, _u16p, _i64, _i64, ctypes.c_float]
+        lib.oracle_residual_layernorm_bf16.argtypes = [_u16p, _u16p, _u16p, _u16p, _u16p, _u16p,
+                                                       _i64, _i64, ctypes.c_float]
+        lib.oracle_cross_entropy_bf16.argtypes = [_u16p, _i32p, _f32p, _i64, _i64]
+        lib.oracle_bf16_from_double.argtypes = [ctypes.c_double]
+        lib.oracle_bf16_from_double.restype = ctypes.c_uint16
         lib.oracle_owner.argtypes = [_i64, _i64, _i64, _i64p, _i64p]
         lib.oracle_owner.restype = None
         lib.oracle_logical_index.argtypes = [_i64, _i64, _i64, _i64]
@@ -77,6 +86,8 @@ def _p(a, t):
 
 
 def _check(rc):
+    if rc == 2:
+        raise MemoryError("oracle scratch allocation failed")
     if rc != 0:
         raise ValueError("oracle rejected the arguments (rows < 0 or cols <= 0)")
 
@@ -117,9 +128,8 @@ def layernorm(x, gamma, beta, eps):
     b = _f32(beta, 1)
     rows, cols = x.shape
     y = np.empty_like(x)
-    scratch = np.empty(cols, np.float64)
     _check(_load().oracle_layernorm_f32(_p(x, _f32p), _p(g, _f32p), _p(b, _f32p), _p(y, _f32p),
-                                        rows, cols, eps, _p(scratch, _f64p)))
+                                        rows, cols, eps))
     return y
 
 
@@ -133,10 +143,9 @@ def residual_layernorm(x, residual, gamma, beta, eps):
     assert r.shape == x.shape
     y = np.empty_like(x)
     h = np.empty_like(x)
-    scratch = np.empty(cols, np.float64)
     _check(_load().oracle_residual_layernorm_f32(_p(x, _f32p), _p(r, _f32p), _p(g, _f32p),
                                                  _p(b, _f32p), _p(y, _f32p), _p(h, _f32p),
-                                                 rows, cols, eps, _p(scratch, _f64p)))
+                                                 rows, cols, eps))
     return y, h
 
 
@@ -148,6 +157,86 @@ def cross_entropy(logits, targets):
     assert t.shape == (rows,)
     loss = np.empty(rows, np.float32)
     _check(_load().oracle_cross_entropy_f32(_p(x, _f32p), _p(t, _i32p), _p(loss, _f32p), rows, cols))
+    return loss
+
+
+# ---- bfloat16 storage (arrays of uint16 bit patterns) -----------------------
+
+def _u16(a, ndim):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bfloat16 data is passed as uint16 bit patterns")
+    if a.ndim != ndim:
+        raise ValueError(f"expected {ndim}-d array, got shape {a.shape}")
+    return a
+
+
+def bf16_from_double(v: float) -> int:
+    """Bit pattern of the bfloat16 nearest to v (ties to even), rounded once."""
+    return int(_load().oracle_bf16_from_double(float(v)))
+
+
+def bf16_to_float(b) -> np.ndarray:
+    """Exact float32 values of bfloat16 bit patterns."""
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def rmsnorm_bf16(x, w, eps):
+    x = _u16(x, 2)
+    w = _u16(w, 1)
+    rows, cols = x.shape
+    y = np.empty_like(x)
+    _check(_load().oracle_rmsnorm_bf16(_p(x, _u16p), _p(w, _u16p), _p(y, _u16p), rows, cols, eps))
+    return y
+
+
+def row_sum_bf16(x):
+    x = _u16(x, 2)
+    rows, cols = x.shape
+    out = np.empty(rows, np.float32)
+    _check(_load().oracle_row_sum_bf16(_p(x, _u16p), _p(out, _f32p), rows, cols))
+    return out
+
+
+def softmax_bf16(x):
+    x = _u16(x, 2)
+    rows, cols = x.shape
+    y = np.empty_like(x)
+    _check(_load().oracle_softmax_bf16(_p(x, _u16p), _p(y, _u16p), rows, cols))
+    return y
+
+
+def layernorm_bf16(x, gamma, beta, eps):
+    x = _u16(x, 2)
+    g = _u16(gamma, 1)
+    b = _u16(beta, 1)
+    rows, cols = x.shape
+    y = np.empty_like(x)
+    _check(_load().oracle_layernorm_bf16(_p(x, _u16p), _p(g, _u16p), _p(b, _u16p), _p(y, _u16p),
+                                         rows, cols, eps))
+    return y
+
+
+def residual_layernorm_bf16(x, residual, gamma, beta, eps):
+    x = _u16(x, 2)
+    r = _u16(residual, 2)
+    g = _u16(gamma, 1)
+    b = _u16(beta, 1)
+    rows, cols = x.shape
+    y = np.empty_like(x)
+    h = np.empty_like(x)
+    _check(_load().oracle_residual_layernorm_bf16(_p(x, _u16p), _p(r, _u16p), _p(g, _u16p),
+                                                  _p(b, _u16p), _p(y, _u16p), _p(h, _u16p),
+                                                  rows, cols, eps))
+    return y, h
+
+
+def cross_entropy_bf16(logits, targets):
+    x = _u16(logits, 2)
+    t = np.ascontiguousarray(targets, dtype=np.int32)
+    rows, cols = x.shape
+    loss = np.empty(rows, np.float32)
+    _check(_load().oracle_cross_entropy_bf16(_p(x, _u16p), _p(t, _i32p), _p(loss, _f32p), rows, cols))
     return loss
 
 

@@ -138,8 +138,36 @@ def config_workloads(k: int, held_out: bool = False, include_large: bool = True)
     raise ValueError(f"no configuration {k}")
 
 
+def as_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of float32 inputs, by torch's conversion
+    (round to nearest even). Used to draw bfloat16 workloads: the float32 draw
+    above, then one conversion."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def family_inputs_bf16(rows: int, cols: int, seed: int) -> dict[str, np.ndarray]:
+    """The family inputs of `family_inputs`, with every float tensor as bfloat16 bits."""
+    d = family_inputs(rows, cols, seed)
+    return {k: (v if k == "targets" else as_bf16_bits(v)) for k, v in d.items()}
+
+
+def rmsnorm_inputs_bf16(rows: int, cols: int, seed: int, outlier_fraction: float = 0.0):
+    """(x, w) of `rmsnorm_workload` as bfloat16 bits."""
+    wl = rmsnorm_workload(rows, cols, seed, outlier_fraction)
+    return as_bf16_bits(wl.x), as_bf16_bits(wl.w)
+
+
 def algorithmic_bytes(op: str, rows: int, cols: int, with_h_out: bool = False) -> int:
-    """Bytes one call must move at minimum: each input read once, each output written once."""
+    """Bytes one call must move at minimum: each input read once, each output
+    written once. A `_bf16` suffix on the op halves the element size of the
+    row and weight tensors (per-row outputs stay float32)."""
+    if op.endswith("_bf16"):
+        base = op[:-5]
+        full = algorithmic_bytes(base, rows, cols, with_h_out)
+        per_row_out = {"sum": 4 * rows, "cross_entropy": 8 * rows}.get(base, 0)
+        return (full - per_row_out) // 2 + per_row_out
     rc = rows * cols
     if op == "rmsnorm":
         return 8 * rc + 4 * cols

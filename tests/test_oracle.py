@@ -293,3 +293,106 @@ def test_page_plans_slot_counts_by_enumeration():
             wk = (i // V) % W            # owner by counting runs of V across W workers
             counts[wk] = counts.get(wk, 0) + 1
         assert oracle.slot_bound(cols, W, V) == max(counts.values())
+
+
+# ---------------------------------------------------------------- bfloat16 storage
+
+def torch_bf16_bits(a32):
+    """torch's float32 -> bfloat16 conversion (round to nearest even)."""
+    t = torch.from_numpy(np.ascontiguousarray(a32, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_ulp(b):
+    """Unit in the last place of bfloat16 values (as float64)."""
+    v = np.abs(oracle.bf16_to_float(b).astype(np.float64))
+    e = np.floor(np.log2(np.maximum(v, 2.0 ** -133)))
+    return np.maximum(2.0 ** (e - 7), 2.0 ** -133)
+
+
+def test_bf16_rounding_matches_torch_on_float32_values():
+    rng = np.random.default_rng(5)
+    vals = [rng.normal(0, 1, 2000), rng.normal(0, 1, 2000) * 10.0 ** rng.integers(-40, 38, 2000),
+            [0.0, -0.0, 1.0, -1.0, 3.0e38, 3.3895313e38, -3.3895313e38, 1e-40, -1e-40, 1.2e-38]]
+    x = np.concatenate([np.asarray(v, np.float64) for v in vals]).astype(np.float32)
+    # Exact ties: a bfloat16 value plus half its quantum (low half 0x8000).
+    base = torch_bf16_bits(rng.normal(0, 1, 500).astype(np.float32)).astype(np.uint32)
+    ties = ((base << 16) | 0x8000).astype(np.uint32).view(np.float32)
+    x = np.concatenate([x, ties, -ties])
+    got = np.array([oracle.bf16_from_double(float(v)) for v in x], np.uint16)
+    assert np.array_equal(got, torch_bf16_bits(x))
+
+
+def test_bf16_rounding_directed_cases():
+    one = 1.0
+    q = 2.0 ** -7                      # quantum of bfloat16 in [1, 2)
+    assert oracle.bf16_from_double(one + q / 2) == 0x3f80          # tie -> even (1.0)
+    assert oracle.bf16_from_double(one + q / 2 + 2.0 ** -40) == 0x3f81  # just above the tie
+    assert oracle.bf16_from_double(one + 1.5 * q) == 0x3f82        # tie -> even (1 + 2q)
+    assert oracle.bf16_from_double(one + 1.5 * q - 2.0 ** -40) == 0x3f81
+    assert oracle.bf16_from_double(2.0 - q / 4) == 0x4000          # rounds up across the binade
+    assert oracle.bf16_from_double(float("inf")) == 0x7f80
+    assert oracle.bf16_from_double(3.5e38) == 0x7f80               # overflow -> inf
+    assert oracle.bf16_from_double(-3.5e38) == 0xff80
+    assert oracle.bf16_from_double(2.0 ** -133) == 0x0001          # smallest subnormal
+    assert oracle.bf16_from_double(2.0 ** -135) == 0x0000          # below half of it
+    assert oracle.bf16_from_double(float("nan")) & 0x7f80 == 0x7f80
+
+
+@pytest.mark.parametrize("cols", [1, 33, 257, 4096])
+def test_bf16_row_sum_and_cross_entropy_equal_f32_oracle_on_widened_inputs(cols):
+    d = workloads.family_inputs_bf16(5, cols, seed=12)
+    x32 = oracle.bf16_to_float(d["x"])
+    assert np.array_equal(oracle.row_sum_bf16(d["x"]), oracle.row_sum(x32))
+    assert np.array_equal(oracle.cross_entropy_bf16(d["x"], d["targets"]),
+                          oracle.cross_entropy(x32, d["targets"]))
+
+
+def _within_bf16_ulp(got_bits, ref64):
+    g = oracle.bf16_to_float(got_bits).astype(np.float64)
+    ref_bits = torch_bf16_bits(ref64.astype(np.float32))
+    ok = np.abs(g - ref64) <= bf16_ulp(ref_bits)
+    exact = np.mean(got_bits == ref_bits)
+    return bool(np.all(ok)), exact
+
+
+@pytest.mark.parametrize("cols", [1, 31, 257, 4096])
+def test_bf16_rmsnorm_softmax_layernorm_match_library_routines(cols):
+    d = workloads.family_inputs_bf16(5, cols, seed=13)
+    x64 = t64(oracle.bf16_to_float(d["x"]))
+    g64 = t64(oracle.bf16_to_float(d["gamma"]))
+    b64 = t64(oracle.bf16_to_float(d["beta"]))
+    eps = float(np.float32(1e-5))
+    cases = [
+        (oracle.rmsnorm_bf16(d["x"], d["gamma"], 1e-5), F.rms_norm(x64, (cols,), weight=g64, eps=eps)),
+        (oracle.softmax_bf16(d["x"]), torch.softmax(x64, dim=1)),
+        (oracle.layernorm_bf16(d["x"], d["gamma"], d["beta"], 1e-5),
+         F.layer_norm(x64, (cols,), g64, b64, eps=eps)),
+    ]
+    for got, ref in cases:
+        ok, exact = _within_bf16_ulp(got, ref.numpy())
+        assert ok and exact > 0.99
+
+
+def test_bf16_residual_layernorm_h_is_one_rounding_of_the_sum():
+    d = workloads.family_inputs_bf16(5, 257, seed=14)
+    y, h = oracle.residual_layernorm_bf16(d["x"], d["residual"], d["gamma"], d["beta"], 1e-5)
+    hs = torch.from_numpy(oracle.bf16_to_float(d["x"])).double() + \
+        torch.from_numpy(oracle.bf16_to_float(d["residual"])).double()
+    assert np.array_equal(h, torch_bf16_bits(hs.float().numpy()))
+    ref = F.layer_norm(torch.from_numpy(oracle.bf16_to_float(h)).double(), (257,),
+                       t64(oracle.bf16_to_float(d["gamma"])), t64(oracle.bf16_to_float(d["beta"])),
+                       eps=float(np.float32(1e-5)))
+    ok, exact = _within_bf16_ulp(y, ref.numpy())
+    assert ok and exact > 0.99
+
+
+def test_bf16_rmsnorm_constant_row_closed_form():
+    c = 0.75
+    w = workloads.as_bf16_bits(np.linspace(0.5, 1.5, 64, dtype=np.float32))
+    x = workloads.as_bf16_bits(np.full((2, 64), c, np.float32))
+    y = oracle.rmsnorm_bf16(x, w, 1e-6)
+    wf = oracle.bf16_to_float(w).astype(np.float64)
+    ref = wf * c / math.sqrt(c * c + float(np.float32(1e-6)))
+    ok, exact = _within_bf16_ulp(y[0], ref)
+    assert ok and np.array_equal(y[0], y[1])
