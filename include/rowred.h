@@ -65,7 +65,14 @@ typedef enum rr_op {
     RR_OP_SOFTMAX = 2,
     RR_OP_LAYERNORM = 3,
     RR_OP_RESIDUAL_LAYERNORM = 4,
-    RR_OP_CROSS_ENTROPY = 5
+    RR_OP_CROSS_ENTROPY = 5,
+    /* The same operators with bfloat16 storage (see the *_bf16 entry points). */
+    RR_OP_RMSNORM_BF16 = 6,
+    RR_OP_SUM_BF16 = 7,
+    RR_OP_SOFTMAX_BF16 = 8,
+    RR_OP_LAYERNORM_BF16 = 9,
+    RR_OP_RESIDUAL_LAYERNORM_BF16 = 10,
+    RR_OP_CROSS_ENTROPY_BF16 = 11
 } rr_op;
 
 /* How rows map onto workgroups.
@@ -91,10 +98,14 @@ typedef enum rr_path {
  *   lanes_per_row   workers per row: power of two, 8..1024, <= block
  *                   (LOOP: equal to block)
  *   rows_per_group  block / lanes_per_row (LOOP: 1)
- *   v               consecutive floats per worker pack: 1, 2 or 4
- *   slots           floats each worker keeps in registers: chunks * v with
- *                   chunks in {1, 2, 4, 8}; cols <= lanes_per_row * slots.
- *                   0 on the LOOP path.
+ *   v               consecutive elements per worker pack: 1, 2 or 4 for
+ *                   float rows; 1, 2, 4 or 8 for bfloat16 rows, where v > 1
+ *                   also needs cols % v == 0 and every tensor pointer
+ *                   aligned to 2*v bytes (one naturally aligned access per
+ *                   pack, at most 16 bytes)
+ *   slots           values each worker keeps in registers: chunks * v with
+ *                   chunks in {1, 2, 4, 8} and slots <= 32;
+ *                   cols <= lanes_per_row * slots. 0 on the LOOP path.
  *   cache           cache policy for the row data: 0 = default; 1 = output
  *                   stores non-temporal; 2 = row loads (x, residual) and
  *                   output stores non-temporal. Weights (w, gamma, beta) are
@@ -163,6 +174,46 @@ int residual_layernorm_f32_ex(const float *x, const float *residual,
                               const rr_plan *plan, void *stream);
 int cross_entropy_f32_ex(const float *logits, const int32_t *targets, float *loss,
                          int64_t rows, int64_t cols, const rr_plan *plan, void *stream);
+
+/* ---- bfloat16 storage ------------------------------------------------------
+ * The same six operators on bfloat16 tensors, passed as uint16_t bit
+ * patterns: inputs are widened exactly to float, every reduction and the
+ * epilogue run in float (row sum in float64), and each element output is
+ * rounded to bfloat16 (nearest, ties to even) once, on the store — the
+ * 16-bit-I/O, FP32-arithmetic form the meTile page measures (section
+ * "Measurements and reproduction"). Weights (w, gamma, beta) are bfloat16 too;
+ * per-row outputs (row sum, loss) are float. Tensor pointers must be at least
+ * 2-byte aligned (else RR_ERR_INVALID_ARGUMENT); the selected plan uses the
+ * widest pack the pointers' alignment allows, and an explicit plan whose v
+ * needs more alignment than the pointers have returns RR_ERR_UNSUPPORTED.
+ * Residual LayerNorm rounds h = x + residual to bfloat16 before normalising
+ * (h materialised at the tensors' precision) and stores that h in h_out. */
+int rmsnorm_bf16(const uint16_t *x, const uint16_t *w, uint16_t *y,
+                 int64_t rows, int64_t cols, float eps, void *stream);
+int row_sum_bf16(const uint16_t *x, float *out, int64_t rows, int64_t cols, void *stream);
+int softmax_bf16(const uint16_t *x, uint16_t *y, int64_t rows, int64_t cols, void *stream);
+int layernorm_bf16(const uint16_t *x, const uint16_t *gamma, const uint16_t *beta, uint16_t *y,
+                   int64_t rows, int64_t cols, float eps, void *stream);
+int residual_layernorm_bf16(const uint16_t *x, const uint16_t *residual,
+                            const uint16_t *gamma, const uint16_t *beta,
+                            uint16_t *y, uint16_t *h_out,
+                            int64_t rows, int64_t cols, float eps, void *stream);
+int cross_entropy_bf16(const uint16_t *logits, const int32_t *targets, float *loss,
+                       int64_t rows, int64_t cols, void *stream);
+int rmsnorm_bf16_ex(const uint16_t *x, const uint16_t *w, uint16_t *y,
+                    int64_t rows, int64_t cols, float eps, const rr_plan *plan, void *stream);
+int row_sum_bf16_ex(const uint16_t *x, float *out, int64_t rows, int64_t cols,
+                    const rr_plan *plan, void *stream);
+int softmax_bf16_ex(const uint16_t *x, uint16_t *y, int64_t rows, int64_t cols,
+                    const rr_plan *plan, void *stream);
+int layernorm_bf16_ex(const uint16_t *x, const uint16_t *gamma, const uint16_t *beta, uint16_t *y,
+                      int64_t rows, int64_t cols, float eps, const rr_plan *plan, void *stream);
+int residual_layernorm_bf16_ex(const uint16_t *x, const uint16_t *residual,
+                               const uint16_t *gamma, const uint16_t *beta,
+                               uint16_t *y, uint16_t *h_out, int64_t rows, int64_t cols, float eps,
+                               const rr_plan *plan, void *stream);
+int cross_entropy_bf16_ex(const uint16_t *logits, const int32_t *targets, float *loss,
+                          int64_t rows, int64_t cols, const rr_plan *plan, void *stream);
 
 /* Plan the library would use for (op, rows, cols): the measured per-shape
  * table entry when one exists, else the built-in rule. Pure host function;

@@ -18,6 +18,8 @@ from ._capi import OP_IDS, RowRedError, rr_plan
 __all__ = [
     "rmsnorm_f32", "row_sum_f32", "softmax_f32", "layernorm_f32",
     "residual_layernorm_f32", "cross_entropy_f32",
+    "rmsnorm_bf16", "row_sum_bf16", "softmax_bf16", "layernorm_bf16",
+    "residual_layernorm_bf16", "cross_entropy_bf16",
     "rr_select_plan", "rr_check_plan", "rr_status_string", "rr_copy_f32", "rr_empty_kernel",
     "rr_plan", "RowRedError", "OP_IDS",
 ]
@@ -34,10 +36,11 @@ def _stream(stream):
     return _torch().cuda.current_stream().cuda_stream
 
 
-def _mat(t, name):
+def _mat(t, name, dtype=None):
     torch = _torch()
-    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda:
-        raise TypeError(f"{name} must be a float32 CUDA/HIP tensor")
+    dtype = dtype or torch.float32
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
+        raise TypeError(f"{name} must be a {dtype} CUDA/HIP tensor")
     if t.dim() != 2 or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous 2-d tensor, got shape {tuple(t.shape)}")
     return t
@@ -56,7 +59,7 @@ def _vec(t, n, name, dtype=None):
 def _out_like(out, x, name):
     if out is None:
         return _torch().empty_like(x)
-    _mat(out, name)
+    _mat(out, name, x.dtype)
     if out.shape != x.shape:
         raise ValueError(f"{name} must have shape {tuple(x.shape)}")
     return out
@@ -156,6 +159,94 @@ def cross_entropy_f32(logits, targets, loss=None, plan=None, stream=None):
     st = _capi.lib().cross_entropy_f32_ex(logits.data_ptr(), targets.data_ptr(), loss.data_ptr(),
                                            rows, cols, _plan_ptr(plan), _stream(stream))
     _capi.check("cross_entropy_f32", st)
+    return loss
+
+
+# ---- bfloat16 storage: float arithmetic, one rounding per stored element -----
+
+def _bf16():
+    return _torch().bfloat16
+
+
+def rmsnorm_bf16(x, w, eps=1e-6, y=None, plan=None, stream=None):
+    """rmsnorm_f32 on bfloat16 x, w, y. Returns y."""
+    _mat(x, "x", _bf16())
+    rows, cols = x.shape
+    _vec(w, cols, "w", _bf16())
+    y = _out_like(y, x, "y")
+    st = _capi.lib().rmsnorm_bf16_ex(x.data_ptr(), w.data_ptr(), y.data_ptr(), rows, cols, float(eps),
+                                      _plan_ptr(plan), _stream(stream))
+    _capi.check("rmsnorm_bf16", st)
+    return y
+
+
+def row_sum_bf16(x, out=None, plan=None, stream=None):
+    """Row sums of bfloat16 x as float32 (float64 accumulation). Returns out."""
+    _mat(x, "x", _bf16())
+    rows, cols = x.shape
+    out = _out_rows(out, x, "out")
+    st = _capi.lib().row_sum_bf16_ex(x.data_ptr(), out.data_ptr(), rows, cols, _plan_ptr(plan),
+                                      _stream(stream))
+    _capi.check("row_sum_bf16", st)
+    return out
+
+
+def softmax_bf16(x, y=None, plan=None, stream=None):
+    """softmax_f32 on bfloat16 x, y. Returns y."""
+    _mat(x, "x", _bf16())
+    rows, cols = x.shape
+    y = _out_like(y, x, "y")
+    st = _capi.lib().softmax_bf16_ex(x.data_ptr(), y.data_ptr(), rows, cols, _plan_ptr(plan),
+                                      _stream(stream))
+    _capi.check("softmax_bf16", st)
+    return y
+
+
+def layernorm_bf16(x, gamma, beta, eps=1e-5, y=None, plan=None, stream=None):
+    """layernorm_f32 on bfloat16 x, gamma, beta, y. Returns y."""
+    _mat(x, "x", _bf16())
+    rows, cols = x.shape
+    _vec(gamma, cols, "gamma", _bf16())
+    _vec(beta, cols, "beta", _bf16())
+    y = _out_like(y, x, "y")
+    st = _capi.lib().layernorm_bf16_ex(x.data_ptr(), gamma.data_ptr(), beta.data_ptr(), y.data_ptr(),
+                                        rows, cols, float(eps), _plan_ptr(plan), _stream(stream))
+    _capi.check("layernorm_bf16", st)
+    return y
+
+
+def residual_layernorm_bf16(x, residual, gamma, beta, eps=1e-5, y=None, h_out=None, plan=None,
+                            stream=None):
+    """h = bf16(x + residual); y = LayerNorm(h), bfloat16 storage. Returns y."""
+    _mat(x, "x", _bf16())
+    rows, cols = x.shape
+    _mat(residual, "residual", _bf16())
+    if residual.shape != x.shape:
+        raise ValueError("residual must have the shape of x")
+    _vec(gamma, cols, "gamma", _bf16())
+    _vec(beta, cols, "beta", _bf16())
+    y = _out_like(y, x, "y")
+    h_ptr = None
+    if h_out is not None:
+        _out_like(h_out, x, "h_out")
+        h_ptr = h_out.data_ptr()
+    st = _capi.lib().residual_layernorm_bf16_ex(x.data_ptr(), residual.data_ptr(), gamma.data_ptr(),
+                                                 beta.data_ptr(), y.data_ptr(), h_ptr, rows, cols,
+                                                 float(eps), _plan_ptr(plan), _stream(stream))
+    _capi.check("residual_layernorm_bf16", st)
+    return y
+
+
+def cross_entropy_bf16(logits, targets, loss=None, plan=None, stream=None):
+    """cross_entropy_f32 on bfloat16 logits; float32 loss. Returns loss."""
+    torch = _torch()
+    _mat(logits, "logits", _bf16())
+    rows, cols = logits.shape
+    _vec(targets, rows, "targets", dtype=torch.int32)
+    loss = _out_rows(loss, logits, "loss")
+    st = _capi.lib().cross_entropy_bf16_ex(logits.data_ptr(), targets.data_ptr(), loss.data_ptr(),
+                                            rows, cols, _plan_ptr(plan), _stream(stream))
+    _capi.check("cross_entropy_bf16", st)
     return loss
 
 

@@ -24,6 +24,7 @@ RR_OP_SOFTMAX = 2
 RR_OP_LAYERNORM = 3
 RR_OP_RESIDUAL_LAYERNORM = 4
 RR_OP_CROSS_ENTROPY = 5
+RR_OP_BF16_OFFSET = 6   # RR_OP_<op>_BF16 = RR_OP_<op> + 6
 
 RR_PATH_PACKED = 0
 RR_PATH_ROW = 1
@@ -37,6 +38,7 @@ OP_IDS = {
     "residual_layernorm": RR_OP_RESIDUAL_LAYERNORM,
     "cross_entropy": RR_OP_CROSS_ENTROPY,
 }
+OP_IDS.update({f"{k}_bf16": v + RR_OP_BF16_OFFSET for k, v in list(OP_IDS.items())})
 
 # Every symbol include/rowred.h declares.
 EXPORTED = (
@@ -44,6 +46,10 @@ EXPORTED = (
     "residual_layernorm_f32", "cross_entropy_f32",
     "rmsnorm_f32_ex", "row_sum_f32_ex", "softmax_f32_ex", "layernorm_f32_ex",
     "residual_layernorm_f32_ex", "cross_entropy_f32_ex",
+    "rmsnorm_bf16", "row_sum_bf16", "softmax_bf16", "layernorm_bf16",
+    "residual_layernorm_bf16", "cross_entropy_bf16",
+    "rmsnorm_bf16_ex", "row_sum_bf16_ex", "softmax_bf16_ex", "layernorm_bf16_ex",
+    "residual_layernorm_bf16_ex", "cross_entropy_bf16_ex",
     "rr_select_plan", "rr_check_plan", "rr_status_string",
     "rr_copy_f32", "rr_empty_kernel",
 )
@@ -89,6 +95,18 @@ _SIGNATURES = {
     "layernorm_f32_ex": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp],
     "residual_layernorm_f32_ex": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp],
     "cross_entropy_f32_ex": [_vp, _vp, _vp, _i64, _i64, _planp, _vp],
+    "rmsnorm_bf16": [_vp, _vp, _vp, _i64, _i64, _f32, _vp],
+    "row_sum_bf16": [_vp, _vp, _i64, _i64, _vp],
+    "softmax_bf16": [_vp, _vp, _i64, _i64, _vp],
+    "layernorm_bf16": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp],
+    "residual_layernorm_bf16": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp],
+    "cross_entropy_bf16": [_vp, _vp, _vp, _i64, _i64, _vp],
+    "rmsnorm_bf16_ex": [_vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp],
+    "row_sum_bf16_ex": [_vp, _vp, _i64, _i64, _planp, _vp],
+    "softmax_bf16_ex": [_vp, _vp, _i64, _i64, _planp, _vp],
+    "layernorm_bf16_ex": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp],
+    "residual_layernorm_bf16_ex": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp],
+    "cross_entropy_bf16_ex": [_vp, _vp, _vp, _i64, _i64, _planp, _vp],
     "rr_select_plan": [ctypes.c_int, _i64, _i64, _planp],
     "rr_check_plan": [ctypes.c_int, _i64, _i64, _planp],
     "rr_status_string": [ctypes.c_int],

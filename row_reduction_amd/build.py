@@ -33,6 +33,12 @@ HIP_SOURCES = [
     "kernels_layernorm.hip",
     "kernels_residual_layernorm.hip",
     "kernels_cross_entropy.hip",
+    "kernels_rmsnorm_bf16.hip",
+    "kernels_row_sum_bf16.hip",
+    "kernels_softmax_bf16.hip",
+    "kernels_layernorm_bf16.hip",
+    "kernels_residual_layernorm_bf16.hip",
+    "kernels_cross_entropy_bf16.hip",
 ]
 CXX_SOURCES = ["plan.cpp"]
 

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "internal.h"
 
 namespace rowred {
@@ -23,15 +25,30 @@ int check_shape(int64_t rows, int64_t cols) {
     return RR_OK;
 }
 
-// Plan for the call: the caller's (checked) or the selector's.
-int resolve_plan(int op, int64_t rows, int64_t cols, const rr_plan *plan, rr_plan *out) {
+// A required bfloat16 pointer: present and 2-byte aligned.
+bool ok_ptr16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
+
+// Widest bfloat16 pack (2V bytes, V <= 8) that the alignment of every given
+// pointer allows; null pointers impose nothing.
+int max_v_for(std::initializer_list<const void *> ptrs) {
+    uintptr_t bits = 0;
+    for (const void *p : ptrs) bits |= reinterpret_cast<uintptr_t>(p);
+    int v = 8;
+    while (v > 1 && (bits & (uintptr_t)(2 * v - 1))) v /= 2;
+    return v;
+}
+
+// Plan for the call: the caller's (checked) or the selector's. max_v bounds
+// the pack width by the pointers' alignment (bfloat16 storage).
+int resolve_plan(int op, int64_t rows, int64_t cols, const rr_plan *plan, rr_plan *out, int max_v = 8) {
     if (plan != nullptr) {
         int st = check_plan(op, rows, cols, plan);
         if (st != RR_OK) return st == RR_ERR_INVALID_ARGUMENT ? RR_ERR_INVALID_ARGUMENT : RR_ERR_UNSUPPORTED;
+        if (plan->v > max_v) return RR_ERR_UNSUPPORTED;
         *out = *plan;
         return RR_OK;
     }
-    return select_plan(op, rows, cols, out);
+    return select_plan(op, rows, cols, out, max_v);
 }
 
 Args base_args(int64_t rows, int64_t cols) {
@@ -177,6 +194,142 @@ int cross_entropy_f32_ex(const float *logits, const int32_t *targets, float *los
 int cross_entropy_f32(const float *logits, const int32_t *targets, float *loss, int64_t rows,
                       int64_t cols, void *stream) {
     return cross_entropy_f32_ex(logits, targets, loss, rows, cols, nullptr, stream);
+}
+
+// ---- bfloat16 storage -----------------------------------------------------------
+
+int rmsnorm_bf16_ex(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t rows, int64_t cols,
+                    float eps, const rr_plan *plan, void *stream) {
+    int st = check_shape(rows, cols);
+    if (st != RR_OK) return st;
+    if (rows == 0) return RR_OK;
+    if (!ok_ptr16(x) || !ok_ptr16(w) || !ok_ptr16(y) || !ok_eps(eps)) return RR_ERR_INVALID_ARGUMENT;
+    rr_plan p;
+    if ((st = resolve_plan(RR_OP_RMSNORM_BF16, rows, cols, plan, &p, max_v_for({x, w, y}))) != RR_OK)
+        return st;
+    Args a = base_args(rows, cols);
+    a.x = x;
+    a.w = w;
+    a.y = y;
+    a.eps = eps;
+    return finish(launch_rmsnorm_bf16(p, a, stream));
+}
+
+int rmsnorm_bf16(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t rows, int64_t cols,
+                 float eps, void *stream) {
+    return rmsnorm_bf16_ex(x, w, y, rows, cols, eps, nullptr, stream);
+}
+
+int row_sum_bf16_ex(const uint16_t *x, float *out, int64_t rows, int64_t cols, const rr_plan *plan,
+                    void *stream) {
+    int st = check_shape(rows, cols);
+    if (st != RR_OK) return st;
+    if (rows == 0) return RR_OK;
+    if (!ok_ptr16(x) || !ok_ptr(out)) return RR_ERR_INVALID_ARGUMENT;
+    rr_plan p;
+    if ((st = resolve_plan(RR_OP_SUM_BF16, rows, cols, plan, &p, max_v_for({x}))) != RR_OK) return st;
+    Args a = base_args(rows, cols);
+    a.x = x;
+    a.row_out = out;
+    return finish(launch_row_sum_bf16(p, a, stream));
+}
+
+int row_sum_bf16(const uint16_t *x, float *out, int64_t rows, int64_t cols, void *stream) {
+    return row_sum_bf16_ex(x, out, rows, cols, nullptr, stream);
+}
+
+int softmax_bf16_ex(const uint16_t *x, uint16_t *y, int64_t rows, int64_t cols, const rr_plan *plan,
+                    void *stream) {
+    int st = check_shape(rows, cols);
+    if (st != RR_OK) return st;
+    if (rows == 0) return RR_OK;
+    if (!ok_ptr16(x) || !ok_ptr16(y)) return RR_ERR_INVALID_ARGUMENT;
+    rr_plan p;
+    if ((st = resolve_plan(RR_OP_SOFTMAX_BF16, rows, cols, plan, &p, max_v_for({x, y}))) != RR_OK) return st;
+    Args a = base_args(rows, cols);
+    a.x = x;
+    a.y = y;
+    return finish(launch_softmax_bf16(p, a, stream));
+}
+
+int softmax_bf16(const uint16_t *x, uint16_t *y, int64_t rows, int64_t cols, void *stream) {
+    return softmax_bf16_ex(x, y, rows, cols, nullptr, stream);
+}
+
+int layernorm_bf16_ex(const uint16_t *x, const uint16_t *gamma, const uint16_t *beta, uint16_t *y,
+                      int64_t rows, int64_t cols, float eps, const rr_plan *plan, void *stream) {
+    int st = check_shape(rows, cols);
+    if (st != RR_OK) return st;
+    if (rows == 0) return RR_OK;
+    if (!ok_ptr16(x) || !ok_ptr16(gamma) || !ok_ptr16(beta) || !ok_ptr16(y) || !ok_eps(eps))
+        return RR_ERR_INVALID_ARGUMENT;
+    rr_plan p;
+    if ((st = resolve_plan(RR_OP_LAYERNORM_BF16, rows, cols, plan, &p, max_v_for({x, gamma, beta, y}))) != RR_OK)
+        return st;
+    Args a = base_args(rows, cols);
+    a.x = x;
+    a.w = gamma;
+    a.beta = beta;
+    a.y = y;
+    a.eps = eps;
+    return finish(launch_layernorm_bf16(p, a, stream));
+}
+
+int layernorm_bf16(const uint16_t *x, const uint16_t *gamma, const uint16_t *beta, uint16_t *y,
+                   int64_t rows, int64_t cols, float eps, void *stream) {
+    return layernorm_bf16_ex(x, gamma, beta, y, rows, cols, eps, nullptr, stream);
+}
+
+int residual_layernorm_bf16_ex(const uint16_t *x, const uint16_t *residual, const uint16_t *gamma,
+                               const uint16_t *beta, uint16_t *y, uint16_t *h_out, int64_t rows,
+                               int64_t cols, float eps, const rr_plan *plan, void *stream) {
+    int st = check_shape(rows, cols);
+    if (st != RR_OK) return st;
+    if (rows == 0) return RR_OK;
+    if (!ok_ptr16(x) || !ok_ptr16(residual) || !ok_ptr16(gamma) || !ok_ptr16(beta) || !ok_ptr16(y) ||
+        !ok_eps(eps) || (h_out != nullptr && !ok_ptr16(h_out)))
+        return RR_ERR_INVALID_ARGUMENT;
+    rr_plan p;
+    if ((st = resolve_plan(RR_OP_RESIDUAL_LAYERNORM_BF16, rows, cols, plan, &p,
+                           max_v_for({x, residual, gamma, beta, y, h_out}))) != RR_OK)
+        return st;
+    Args a = base_args(rows, cols);
+    a.x = x;
+    a.residual = residual;
+    a.w = gamma;
+    a.beta = beta;
+    a.y = y;
+    a.h_out = h_out;
+    a.eps = eps;
+    return finish(launch_residual_layernorm_bf16(p, a, stream));
+}
+
+int residual_layernorm_bf16(const uint16_t *x, const uint16_t *residual, const uint16_t *gamma,
+                            const uint16_t *beta, uint16_t *y, uint16_t *h_out, int64_t rows,
+                            int64_t cols, float eps, void *stream) {
+    return residual_layernorm_bf16_ex(x, residual, gamma, beta, y, h_out, rows, cols, eps, nullptr,
+                                      stream);
+}
+
+int cross_entropy_bf16_ex(const uint16_t *logits, const int32_t *targets, float *loss, int64_t rows,
+                          int64_t cols, const rr_plan *plan, void *stream) {
+    int st = check_shape(rows, cols);
+    if (st != RR_OK) return st;
+    if (rows == 0) return RR_OK;
+    if (!ok_ptr16(logits) || !ok_ptr(targets) || !ok_ptr(loss)) return RR_ERR_INVALID_ARGUMENT;
+    rr_plan p;
+    if ((st = resolve_plan(RR_OP_CROSS_ENTROPY_BF16, rows, cols, plan, &p, max_v_for({logits}))) != RR_OK)
+        return st;
+    Args a = base_args(rows, cols);
+    a.x = logits;
+    a.targets = targets;
+    a.row_out = loss;
+    return finish(launch_cross_entropy_bf16(p, a, stream));
+}
+
+int cross_entropy_bf16(const uint16_t *logits, const int32_t *targets, float *loss, int64_t rows,
+                       int64_t cols, void *stream) {
+    return cross_entropy_bf16_ex(logits, targets, loss, rows, cols, nullptr, stream);
 }
 
 int rr_select_plan(int op, int64_t rows, int64_t cols, rr_plan *out) {

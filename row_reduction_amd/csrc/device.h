@@ -38,10 +38,24 @@ namespace rowred {
 
 enum OpId { kRmsNorm = 0, kSum = 1, kSoftmax = 2, kLayerNorm = 3, kResidualLayerNorm = 4, kCrossEntropy = 5 };
 
-// V consecutive floats at 4-byte alignment. Row origins of odd-width rows are
-// only dword aligned; gfx9 vector memory instructions accept that.
+// Storage types. float rows: packs of V consecutive floats at 4-byte
+// alignment (row origins of odd-width rows are only dword aligned; gfx9
+// vector memory instructions accept that). bfloat16 rows: packs of V
+// bfloat16 loaded as 2V bytes with natural alignment (the planner admits
+// V > 1 only when cols is a multiple of V and the pointers are 2V-byte
+// aligned), widened to float exactly, and rounded back to nearest-even on
+// the store (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16_t;
 typedef float f32x2u __attribute__((ext_vector_type(2), aligned(4)));
 typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+typedef unsigned short u16;
+typedef unsigned int u32;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <class T>
+constexpr bool is_bf16 = __is_same(T, bf16_t);
 
 // Cache policy of a launch (rr_plan.cache): rows are touched once, so their
 // loads and stores may carry the non-temporal ("nt") hint, which keeps them
@@ -53,8 +67,8 @@ constexpr int kHintNtStore = 1;
 constexpr int kHintNtLoad = 2;
 constexpr int hint_of_cache(int cache) { return cache == 0 ? 0 : (cache == 1 ? kHintNtStore : kHintNtStore | kHintNtLoad); }
 
-// Overloads on the dword-aligned types (a template over the value type would
-// lose the typedefs' 4-byte alignment and assume natural vector alignment).
+// Overloads per access type (a template over the value type would lose the
+// float typedefs' 4-byte alignment and assume natural vector alignment).
 #define ROWRED_LDST(T)                                                                    \
     template <int HINT, bool STREAM>                                                      \
     __device__ __forceinline__ T ld(const T *p) {                                         \
@@ -69,7 +83,24 @@ constexpr int hint_of_cache(int cache) { return cache == 0 ? 0 : (cache == 1 ? k
 ROWRED_LDST(float)
 ROWRED_LDST(f32x2u)
 ROWRED_LDST(f32x4u)
+ROWRED_LDST(u16)
+ROWRED_LDST(u32)
+ROWRED_LDST(u32x2)
+ROWRED_LDST(u32x4)
 #undef ROWRED_LDST
+
+// bfloat16 <-> float: widening is exact (the bits are the float's top half).
+__device__ __forceinline__ float bf16_lo(u32 u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16_hi(u32 u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+__device__ __forceinline__ u32 pack_bf16(float a, float b) {
+    bf16x2 v;
+    v.x = (bf16_t)a;
+    v.y = (bf16_t)b;
+    return __builtin_bit_cast(u32, v);
+}
+__device__ __forceinline__ u16 bf16_bits(float a) { return __builtin_bit_cast(u16, (bf16_t)a); }
+// The float value of `a` rounded to bfloat16.
+__device__ __forceinline__ float round_to_bf16(float a) { return __builtin_bit_cast(float, (u32)bf16_bits(a) << 16); }
 
 template <int V, int HINT = 0, bool STREAM = false>
 __device__ __forceinline__ void load_pack(const float *__restrict__ p, float *d) {
@@ -80,12 +111,40 @@ __device__ __forceinline__ void load_pack(const float *__restrict__ p, float *d)
         d[0] = t.x;
         d[1] = t.y;
     } else {
-        static_assert(V == 4, "V must be 1, 2 or 4");
+        static_assert(V == 4, "float rows: V must be 1, 2 or 4");
         f32x4u t = ld<HINT, STREAM>(reinterpret_cast<const f32x4u *>(p));
         d[0] = t.x;
         d[1] = t.y;
         d[2] = t.z;
         d[3] = t.w;
+    }
+}
+
+template <int V, int HINT = 0, bool STREAM = false>
+__device__ __forceinline__ void load_pack(const bf16_t *__restrict__ p, float *d) {
+    if constexpr (V == 1) {
+        d[0] = __builtin_bit_cast(float, (u32)ld<HINT, STREAM>(reinterpret_cast<const u16 *>(p)) << 16);
+    } else if constexpr (V == 2) {
+        const u32 t = ld<HINT, STREAM>(reinterpret_cast<const u32 *>(p));
+        d[0] = bf16_lo(t);
+        d[1] = bf16_hi(t);
+    } else if constexpr (V == 4) {
+        const u32x2 t = ld<HINT, STREAM>(reinterpret_cast<const u32x2 *>(p));
+        d[0] = bf16_lo(t.x);
+        d[1] = bf16_hi(t.x);
+        d[2] = bf16_lo(t.y);
+        d[3] = bf16_hi(t.y);
+    } else {
+        static_assert(V == 8, "bfloat16 rows: V must be 1, 2, 4 or 8");
+        const u32x4 t = ld<HINT, STREAM>(reinterpret_cast<const u32x4 *>(p));
+        d[0] = bf16_lo(t.x);
+        d[1] = bf16_hi(t.x);
+        d[2] = bf16_lo(t.y);
+        d[3] = bf16_hi(t.y);
+        d[4] = bf16_lo(t.z);
+        d[5] = bf16_hi(t.z);
+        d[6] = bf16_lo(t.w);
+        d[7] = bf16_hi(t.w);
     }
 }
 
@@ -99,6 +158,7 @@ __device__ __forceinline__ void store_pack(float *__restrict__ p, const float *d
         t.y = d[1];
         st<HINT>(reinterpret_cast<f32x2u *>(p), t);
     } else {
+        static_assert(V == 4, "float rows: V must be 1, 2 or 4");
         f32x4u t;
         t.x = d[0];
         t.y = d[1];
@@ -108,16 +168,44 @@ __device__ __forceinline__ void store_pack(float *__restrict__ p, const float *d
     }
 }
 
+template <int V, int HINT = 0>
+__device__ __forceinline__ void store_pack(bf16_t *__restrict__ p, const float *d) {
+    if constexpr (V == 1) {
+        st<HINT>(reinterpret_cast<u16 *>(p), bf16_bits(d[0]));
+    } else if constexpr (V == 2) {
+        st<HINT>(reinterpret_cast<u32 *>(p), pack_bf16(d[0], d[1]));
+    } else if constexpr (V == 4) {
+        u32x2 t;
+        t.x = pack_bf16(d[0], d[1]);
+        t.y = pack_bf16(d[2], d[3]);
+        st<HINT>(reinterpret_cast<u32x2 *>(p), t);
+    } else {
+        static_assert(V == 8, "bfloat16 rows: V must be 1, 2, 4 or 8");
+        u32x4 t;
+        t.x = pack_bf16(d[0], d[1]);
+        t.y = pack_bf16(d[2], d[3]);
+        t.z = pack_bf16(d[4], d[5]);
+        t.w = pack_bf16(d[6], d[7]);
+        st<HINT>(reinterpret_cast<u32x4 *>(p), t);
+    }
+}
+
+template <int HINT>
+__device__ __forceinline__ void store_one(float *p, float v) { st<HINT>(p, v); }
+template <int HINT>
+__device__ __forceinline__ void store_one(bf16_t *p, float v) { st<HINT>(reinterpret_cast<u16 *>(p), bf16_bits(v)); }
+
 // Pack of V columns starting at i0 of a row with `cols` columns (cols >= V),
 // without branches: the V-wide load always reads the in-bounds window that
 // starts at min(i0, cols - V), and each slot then picks its column out of
 // the window, or `fill` when the column lies past the row end. A complete
 // pack reads exactly its own columns; nothing outside the row is read.
-template <int V, int HINT = 0, bool STREAM = false>
-__device__ __forceinline__ void load_window(const float *__restrict__ row, int i0, int cols, float *d,
+template <int V, int HINT = 0, bool STREAM = false, class T>
+__device__ __forceinline__ void load_window(const T *__restrict__ row, int i0, int cols, float *d,
                                             float fill) {
     if constexpr (V == 1) {
-        const float t = ld<HINT, STREAM>(row + (i0 < cols ? i0 : cols - 1));
+        float t;
+        load_pack<1, HINT, STREAM>(row + (i0 < cols ? i0 : cols - 1), &t);
         d[0] = (i0 < cols) ? t : fill;
     } else {
         const int start = i0 < cols - V ? i0 : cols - V;
@@ -136,28 +224,28 @@ __device__ __forceinline__ void load_window(const float *__restrict__ row, int i
 }
 
 // Store of the columns of a pack that lie inside the row.
-template <int V, int HINT = 0>
-__device__ __forceinline__ void store_guarded(float *__restrict__ row, int i0, int cols, const float *d) {
+template <int V, int HINT = 0, class T>
+__device__ __forceinline__ void store_guarded(T *__restrict__ row, int i0, int cols, const float *d) {
     if (i0 + V <= cols) {
         store_pack<V, HINT>(row + i0, d);
     } else {
 #pragma unroll
         for (int e = 0; e < V; ++e)
-            if (i0 + e < cols) st<HINT>(row + i0 + e, d[e]);
+            if (i0 + e < cols) store_one<HINT>(row + i0 + e, d[e]);
     }
 }
 
 // Load / store of one pack: plain V-wide access when the row is an exact
 // multiple of the plan's span (every pack complete), else the guarded forms.
-template <int V, bool EXACT, int HINT = 0, bool STREAM = false>
-__device__ __forceinline__ void load_slots(const float *__restrict__ row, int i0, int cols, float *d,
+template <int V, bool EXACT, int HINT = 0, bool STREAM = false, class T>
+__device__ __forceinline__ void load_slots(const T *__restrict__ row, int i0, int cols, float *d,
                                            float fill) {
     if constexpr (EXACT) load_pack<V, HINT, STREAM>(row + i0, d);
     else load_window<V, HINT, STREAM>(row, i0, cols, d, fill);
 }
 
-template <int V, bool EXACT, int HINT = 0>
-__device__ __forceinline__ void store_slots(float *__restrict__ row, int i0, int cols, const float *d) {
+template <int V, bool EXACT, int HINT = 0, class T>
+__device__ __forceinline__ void store_slots(T *__restrict__ row, int i0, int cols, const float *d) {
     if constexpr (EXACT) store_pack<V, HINT>(row + i0, d);
     else store_guarded<V, HINT>(row, i0, cols, d);
 }
@@ -301,10 +389,17 @@ __device__ __forceinline__ T row_reduce(T v, Op op, const RowLanes<SEG> &rl, T *
 // live floats); SEG: lanes per row when < 64 (several rows per wavefront), or
 // 64 when a row takes lanes_per_row / 64 whole wavefronts; EXACT: the row
 // length equals lanes_per_row * K, so every pack is complete; HINT: cache
-// policy bits (see hint_of_cache).
-template <int OP, int V, int NCHUNK, int SEG, bool EXACT, int HINT>
+// policy bits (see hint_of_cache); T: storage type of rows and weights
+// (float or bfloat16; arithmetic is float either way).
+template <int OP, int V, int NCHUNK, int SEG, bool EXACT, int HINT, class T>
 __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
     constexpr int K = V * NCHUNK;
+    const T *X = static_cast<const T *>(a.x);
+    const T *R = static_cast<const T *>(a.residual);
+    const T *Wt = static_cast<const T *>(a.w);
+    const T *B = static_cast<const T *>(a.beta);
+    T *Y = static_cast<T *>(a.y);
+    T *H = static_cast<T *>(a.h_out);
     constexpr bool kMaxFirst = (OP == kSoftmax || OP == kCrossEntropy);
     __shared__ float lds0[16];
     __shared__ float lds1[16];
@@ -326,24 +421,26 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
     float x_target = 0.0f;
     if constexpr (OP == kCrossEntropy) {
         const int t = a.targets[row];
-        x_target = (t >= 0 && t < cols) ? a.x[off + t] : __builtin_nanf("");
+        x_target = __builtin_nanf("");
+        if (t >= 0 && t < cols) load_pack<1>(X + off + t, &x_target);
     }
 
     // ---- load: the worker's K floats stay in registers until the store.
     float v[K];
 #pragma unroll
     for (int c = 0; c < NCHUNK; ++c)
-        load_slots<V, EXACT, HINT, true>(a.x + off, c * stride + base, cols, &v[c * V], fill);
+        load_slots<V, EXACT, HINT, true>(X + off, c * stride + base, cols, &v[c * V], fill);
     if constexpr (OP == kResidualLayerNorm) {
         float r[K];
 #pragma unroll
         for (int c = 0; c < NCHUNK; ++c)
-            load_slots<V, EXACT, HINT, true>(a.residual + off, c * stride + base, cols, &r[c * V], 0.0f);
+            load_slots<V, EXACT, HINT, true>(R + off, c * stride + base, cols, &r[c * V], 0.0f);
+        // h = x + residual at the tensors' precision (bfloat16 rows round it).
 #pragma unroll
-        for (int k = 0; k < K; ++k) v[k] = v[k] + r[k];
-        if (a.h_out != nullptr && row_ok) {
+        for (int k = 0; k < K; ++k) v[k] = is_bf16<T> ? round_to_bf16(v[k] + r[k]) : v[k] + r[k];
+        if (H != nullptr && row_ok) {
 #pragma unroll
-            for (int c = 0; c < NCHUNK; ++c) store_slots<V, EXACT, HINT>(a.h_out + off, c * stride + base, cols, &v[c * V]);
+            for (int c = 0; c < NCHUNK; ++c) store_slots<V, EXACT, HINT>(H + off, c * stride + base, cols, &v[c * V]);
         }
     }
 
@@ -352,7 +449,7 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
         // the reduction; the epilogue then only multiplies and stores.
         float wv[K];
 #pragma unroll
-        for (int c = 0; c < NCHUNK; ++c) load_slots<V, EXACT>(a.w, c * stride + base, cols, &wv[c * V], 0.0f);
+        for (int c = 0; c < NCHUNK; ++c) load_slots<V, EXACT>(Wt, c * stride + base, cols, &wv[c * V], 0.0f);
         float t[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) t[k] = v[k] * v[k];
@@ -364,7 +461,7 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
                 float o[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e) o[e] = v[c * V + e] * inv * wv[c * V + e];
-                store_slots<V, EXACT, HINT>(a.y + off, c * stride + base, cols, o);
+                store_slots<V, EXACT, HINT>(Y + off, c * stride + base, cols, o);
             }
         }
     } else if constexpr (OP == kSum) {
@@ -392,7 +489,7 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
                     float o[V];
 #pragma unroll
                     for (int e = 0; e < V; ++e) o[e] = v[c * V + e] * rz;
-                    store_slots<V, EXACT, HINT>(a.y + off, c * stride + base, cols, o);
+                    store_slots<V, EXACT, HINT>(Y + off, c * stride + base, cols, o);
                 }
             }
         } else {
@@ -422,15 +519,15 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
             float g[K], b[K];
 #pragma unroll
             for (int c = 0; c < NCHUNK; ++c) {
-                load_slots<V, EXACT>(a.w, c * stride + base, cols, &g[c * V], 0.0f);
-                load_slots<V, EXACT>(a.beta, c * stride + base, cols, &b[c * V], 0.0f);
+                load_slots<V, EXACT>(Wt, c * stride + base, cols, &g[c * V], 0.0f);
+                load_slots<V, EXACT>(B, c * stride + base, cols, &b[c * V], 0.0f);
             }
 #pragma unroll
             for (int c = 0; c < NCHUNK; ++c) {
                 float o[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e) o[e] = v[c * V + e] * rstd * g[c * V + e] + b[c * V + e];
-                store_slots<V, EXACT, HINT>(a.y + off, c * stride + base, cols, o);
+                store_slots<V, EXACT, HINT>(Y + off, c * stride + base, cols, o);
             }
         }
     }
@@ -441,8 +538,11 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
 // One row per workgroup, W = blockDim.x workers, the same ownership map with as
 // many chunks as the row needs. Every pass re-reads the row from memory, one
 // branch-free window load per pack.
-template <int OP, int V, int HINT>
+template <int OP, int V, int HINT, class T>
 __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
+    const T *Wt = static_cast<const T *>(a.w);
+    const T *B = static_cast<const T *>(a.beta);
+    T *Y = static_cast<T *>(a.y);
     __shared__ float lds0[16];
     __shared__ float lds1[16];
     __shared__ double ldsd[16];
@@ -453,16 +553,17 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
     const int stride = rl.W * V;
     const int base = rl.lane * V;
     const int nchunk = (cols + stride - 1) / stride;
-    const float *xr = a.x + off;
+    const T *xr = static_cast<const T *>(a.x) + off;
+    const T *rr = (OP == kResidualLayerNorm) ? static_cast<const T *>(a.residual) + off : nullptr;
 
     // Pack of the row's values (x, or x + residual for residual LayerNorm).
     auto read = [&](int i0, float *d, float fill) {
         load_window<V, HINT, true>(xr, i0, cols, d, fill);
         if constexpr (OP == kResidualLayerNorm) {
             float r[V];
-            load_window<V, HINT, true>(a.residual + off, i0, cols, r, 0.0f);
+            load_window<V, HINT, true>(rr, i0, cols, r, 0.0f);
 #pragma unroll
-            for (int e = 0; e < V; ++e) d[e] = d[e] + r[e];
+            for (int e = 0; e < V; ++e) d[e] = is_bf16<T> ? round_to_bf16(d[e] + r[e]) : d[e] + r[e];
         }
     };
 
@@ -481,10 +582,10 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
             const int i0 = c * stride + base;
             float d[V], wv[V];
             read(i0, d, 0.0f);
-            load_window<V>(a.w, i0, cols, wv, 0.0f);
+            load_window<V>(Wt, i0, cols, wv, 0.0f);
 #pragma unroll
             for (int e = 0; e < V; ++e) d[e] = d[e] * inv * wv[e];
-            store_guarded<V, HINT>(a.y + off, i0, cols, d);
+            store_guarded<V, HINT>(Y + off, i0, cols, d);
         }
     } else if constexpr (OP == kSum) {
         double acc = 0.0;
@@ -523,12 +624,13 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
                 read(i0, d, -INFINITY);
 #pragma unroll
                 for (int e = 0; e < V; ++e) d[e] = expf(d[e] - m) * rz;
-                store_guarded<V, HINT>(a.y + off, i0, cols, d);
+                store_guarded<V, HINT>(Y + off, i0, cols, d);
             }
         } else {
             if (rl.lane == 0) {
                 const int t = a.targets[row];
-                const float xt = (t >= 0 && t < cols) ? xr[t] : __builtin_nanf("");
+                float xt = __builtin_nanf("");
+                if (t >= 0 && t < cols) load_pack<1>(xr + t, &xt);
                 a.row_out[row] = logf(z) + m - xt;
             }
         }
@@ -555,17 +657,17 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
         }
         const float var = row_reduce(acc2, AddOp{}, rl, lds1) / (float)cols;
         const float rstd = rsqrtf(var + a.eps);
-        float *hr = (OP == kResidualLayerNorm && a.h_out != nullptr) ? a.h_out + off : nullptr;
+        T *hr = (OP == kResidualLayerNorm && a.h_out != nullptr) ? static_cast<T *>(a.h_out) + off : nullptr;
         for (int c = 0; c < nchunk; ++c) {
             const int i0 = c * stride + base;
             float d[V], g[V], b[V];
             read(i0, d, 0.0f);
             if (hr != nullptr) store_guarded<V, HINT>(hr, i0, cols, d);
-            load_window<V>(a.w, i0, cols, g, 0.0f);
-            load_window<V>(a.beta, i0, cols, b, 0.0f);
+            load_window<V>(Wt, i0, cols, g, 0.0f);
+            load_window<V>(B, i0, cols, b, 0.0f);
 #pragma unroll
             for (int e = 0; e < V; ++e) d[e] = (d[e] - mean) * rstd * g[e] + b[e];
-            store_guarded<V, HINT>(a.y + off, i0, cols, d);
+            store_guarded<V, HINT>(Y + off, i0, cols, d);
         }
     }
 }
@@ -579,57 +681,64 @@ struct Launch {
     int cache;
 };
 
-template <int OP, int V, int NCHUNK, int SEG, bool EXACT>
+template <int OP, int V, int NCHUNK, int SEG, bool EXACT, class T>
 int launch_reg_exact(const Args &a, const Launch &l) {
     switch (l.cache) {
-        case 0: hipLaunchKernelGGL((reg_kernel<OP, V, NCHUNK, SEG, EXACT, hint_of_cache(0)>), l.grid, l.block, 0, l.stream, a); break;
-        case 1: hipLaunchKernelGGL((reg_kernel<OP, V, NCHUNK, SEG, EXACT, hint_of_cache(1)>), l.grid, l.block, 0, l.stream, a); break;
-        case 2: hipLaunchKernelGGL((reg_kernel<OP, V, NCHUNK, SEG, EXACT, hint_of_cache(2)>), l.grid, l.block, 0, l.stream, a); break;
+        case 0: hipLaunchKernelGGL((reg_kernel<OP, V, NCHUNK, SEG, EXACT, hint_of_cache(0), T>), l.grid, l.block, 0, l.stream, a); break;
+        case 1: hipLaunchKernelGGL((reg_kernel<OP, V, NCHUNK, SEG, EXACT, hint_of_cache(1), T>), l.grid, l.block, 0, l.stream, a); break;
+        case 2: hipLaunchKernelGGL((reg_kernel<OP, V, NCHUNK, SEG, EXACT, hint_of_cache(2), T>), l.grid, l.block, 0, l.stream, a); break;
         default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();
 }
 
-template <int OP, int V, int NCHUNK, int SEG>
+template <int OP, int V, int NCHUNK, int SEG, class T>
 int launch_reg(const Args &a, const Launch &l) {
-    return l.exact ? launch_reg_exact<OP, V, NCHUNK, SEG, true>(a, l)
-                   : launch_reg_exact<OP, V, NCHUNK, SEG, false>(a, l);
+    return l.exact ? launch_reg_exact<OP, V, NCHUNK, SEG, true, T>(a, l)
+                   : launch_reg_exact<OP, V, NCHUNK, SEG, false, T>(a, l);
 }
 
-template <int OP, int V, int SEG>
+// Chunk counts with at most 32 live values per lane.
+template <int OP, int V, int SEG, class T>
 int launch_by_chunks(int chunks, const Args &a, const Launch &l) {
     switch (chunks) {
-        case 1: return launch_reg<OP, V, 1, SEG>(a, l);
-        case 2: return launch_reg<OP, V, 2, SEG>(a, l);
-        case 4: return launch_reg<OP, V, 4, SEG>(a, l);
-        case 8: return launch_reg<OP, V, 8, SEG>(a, l);
+        case 1: return launch_reg<OP, V, 1, SEG, T>(a, l);
+        case 2: return launch_reg<OP, V, 2, SEG, T>(a, l);
+        case 4: return launch_reg<OP, V, 4, SEG, T>(a, l);
+        case 8:
+            if constexpr (V * 8 <= 32) return launch_reg<OP, V, 8, SEG, T>(a, l);
+            else return (int)hipErrorInvalidValue;
         default: return (int)hipErrorInvalidValue;
     }
 }
 
-template <int OP, int SEG>
+// V = 1, 2, 4 for float rows; 1, 2, 4, 8 for bfloat16 rows (16 bytes at most).
+template <int OP, int SEG, class T>
 int launch_by_v(int v, int chunks, const Args &a, const Launch &l) {
     switch (v) {
-        case 1: return launch_by_chunks<OP, 1, SEG>(chunks, a, l);
-        case 2: return launch_by_chunks<OP, 2, SEG>(chunks, a, l);
-        case 4: return launch_by_chunks<OP, 4, SEG>(chunks, a, l);
+        case 1: return launch_by_chunks<OP, 1, SEG, T>(chunks, a, l);
+        case 2: return launch_by_chunks<OP, 2, SEG, T>(chunks, a, l);
+        case 4: return launch_by_chunks<OP, 4, SEG, T>(chunks, a, l);
+        case 8:
+            if constexpr (is_bf16<T>) return launch_by_chunks<OP, 8, SEG, T>(chunks, a, l);
+            else return (int)hipErrorInvalidValue;
         default: return (int)hipErrorInvalidValue;
     }
 }
 
-template <int OP, int V>
+template <int OP, int V, class T>
 int launch_loop(const Args &a, const Launch &l) {
     switch (l.cache) {
-        case 0: hipLaunchKernelGGL((loop_kernel<OP, V, hint_of_cache(0)>), l.grid, l.block, 0, l.stream, a); break;
-        case 1: hipLaunchKernelGGL((loop_kernel<OP, V, hint_of_cache(1)>), l.grid, l.block, 0, l.stream, a); break;
-        case 2: hipLaunchKernelGGL((loop_kernel<OP, V, hint_of_cache(2)>), l.grid, l.block, 0, l.stream, a); break;
+        case 0: hipLaunchKernelGGL((loop_kernel<OP, V, hint_of_cache(0), T>), l.grid, l.block, 0, l.stream, a); break;
+        case 1: hipLaunchKernelGGL((loop_kernel<OP, V, hint_of_cache(1), T>), l.grid, l.block, 0, l.stream, a); break;
+        case 2: hipLaunchKernelGGL((loop_kernel<OP, V, hint_of_cache(2), T>), l.grid, l.block, 0, l.stream, a); break;
         default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();
 }
 
-// Launch `OP` with a plan already checked by the planner.
-template <int OP>
+// Launch `OP` on storage type T with a plan already checked by the planner.
+template <int OP, class T>
 int launch_op(const rr_plan &p, const Args &args, void *stream) {
     Args a = args;
     a.lanes_per_row = p.lanes_per_row;
@@ -644,18 +753,21 @@ int launch_op(const rr_plan &p, const Args &args, void *stream) {
     l.cache = p.cache;
     if (p.path == RR_PATH_LOOP) {
         switch (p.v) {
-            case 1: return launch_loop<OP, 1>(a, l);
-            case 2: return launch_loop<OP, 2>(a, l);
-            case 4: return launch_loop<OP, 4>(a, l);
+            case 1: return launch_loop<OP, 1, T>(a, l);
+            case 2: return launch_loop<OP, 2, T>(a, l);
+            case 4: return launch_loop<OP, 4, T>(a, l);
+            case 8:
+                if constexpr (is_bf16<T>) return launch_loop<OP, 8, T>(a, l);
+                else return (int)hipErrorInvalidValue;
             default: return (int)hipErrorInvalidValue;
         }
     }
     const int chunks = p.slots / p.v;
     switch (p.lanes_per_row) {
-        case 8: return launch_by_v<OP, 8>(p.v, chunks, a, l);
-        case 16: return launch_by_v<OP, 16>(p.v, chunks, a, l);
-        case 32: return launch_by_v<OP, 32>(p.v, chunks, a, l);
-        default: return launch_by_v<OP, 64>(p.v, chunks, a, l);
+        case 8: return launch_by_v<OP, 8, T>(p.v, chunks, a, l);
+        case 16: return launch_by_v<OP, 16, T>(p.v, chunks, a, l);
+        case 32: return launch_by_v<OP, 32, T>(p.v, chunks, a, l);
+        default: return launch_by_v<OP, 64, T>(p.v, chunks, a, l);
     }
 }
 

@@ -8,14 +8,16 @@
 namespace rowred {
 
 // Everything one launch needs, passed by value as the kernel argument.
+// Row and weight tensors are float or bfloat16 (the kernel instance decides);
+// per-row outputs are always float.
 struct Args {
-    const float *x;          // input rows (logits for cross-entropy)
-    const float *residual;   // residual LayerNorm second input, else null
-    const float *w;          // RMSNorm weight / LayerNorm gamma, else null
-    const float *beta;       // LayerNorm beta, else null
+    const void *x;           // input rows (logits for cross-entropy)
+    const void *residual;    // residual LayerNorm second input, else null
+    const void *w;           // RMSNorm weight / LayerNorm gamma, else null
+    const void *beta;        // LayerNorm beta, else null
     const int32_t *targets;  // cross-entropy targets, else null
-    float *y;                // per-element output, else null
-    float *h_out;            // residual LayerNorm h = x + residual, may be null
+    void *y;                 // per-element output, else null
+    void *h_out;             // residual LayerNorm h = x + residual, may be null
     float *row_out;          // per-row output (row sum, loss), else null
     int64_t rows;
     int32_t cols;
@@ -33,9 +35,16 @@ int launch_softmax(const rr_plan &p, const Args &a, void *stream);
 int launch_layernorm(const rr_plan &p, const Args &a, void *stream);
 int launch_residual_layernorm(const rr_plan &p, const Args &a, void *stream);
 int launch_cross_entropy(const rr_plan &p, const Args &a, void *stream);
+int launch_rmsnorm_bf16(const rr_plan &p, const Args &a, void *stream);
+int launch_row_sum_bf16(const rr_plan &p, const Args &a, void *stream);
+int launch_softmax_bf16(const rr_plan &p, const Args &a, void *stream);
+int launch_layernorm_bf16(const rr_plan &p, const Args &a, void *stream);
+int launch_residual_layernorm_bf16(const rr_plan &p, const Args &a, void *stream);
+int launch_cross_entropy_bf16(const rr_plan &p, const Args &a, void *stream);
 
 // Planner (plan.cpp; pure host C++).
-int select_plan(int op, int64_t rows, int64_t cols, rr_plan *out);
+// max_v: widest pack the caller's pointer alignment allows (bfloat16 ops).
+int select_plan(int op, int64_t rows, int64_t cols, rr_plan *out, int max_v = 8);
 int check_plan(int op, int64_t rows, int64_t cols, const rr_plan *plan);
 
 }  // namespace rowred

@@ -18,6 +18,7 @@ PACKED_LANES = (8, 16, 32)
 PACKED_BLOCKS = (64, 256)
 ROW_LANES = (64, 128, 256, 512, 1024)
 VS = (1, 2, 4)
+VS_BF16 = (1, 2, 4, 8)
 CHUNKS = (1, 2, 4, 8)
 LOOP_BLOCKS = (256, 1024)
 CACHES = (0, 1, 2)
@@ -44,22 +45,23 @@ def candidate_plans(op: str, rows: int, cols: int, include_loop: bool = True,
             if L.rr_check_plan(op_id, rows, cols, q) == RR_OK:
                 out.append(q)
 
+    vs = VS_BF16 if op.endswith("_bf16") else VS
     for lanes in PACKED_LANES:
         for block in PACKED_BLOCKS:
-            for v in VS:
+            for v in vs:
                 c = _min_chunks(cols, lanes, v)
                 if c is not None:
                     add(rr_plan(RR_PATH_PACKED, block, lanes, block // lanes, v, c * v))
     for lanes in ROW_LANES:
         blocks = sorted({lanes, max(lanes, 256)})
         for block in blocks:
-            for v in VS:
+            for v in vs:
                 c = _min_chunks(cols, lanes, v)
                 if c is not None:
                     add(rr_plan(RR_PATH_ROW, block, lanes, block // lanes, v, c * v))
     if include_loop:
         for block in LOOP_BLOCKS:
-            for v in VS:
+            for v in vs:
                 add(rr_plan(RR_PATH_LOOP, block, block, 1, v, 0))
     return out
 

@@ -54,6 +54,8 @@ def test_status_strings(L):
 
 def call(L, op, x=P, rows=4, cols=8, eps=1e-6, plan=None, **kw):
     """Invoke one entry point with stand-in pointers, overriding some."""
+    if op.endswith("_bf16"):
+        return call_bf16(L, op[:-5], x, rows, cols, eps, plan, **kw)
     if op == "rmsnorm":
         return L.rmsnorm_f32_ex(x, kw.get("w", P), kw.get("y", P), rows, cols, eps, plan, None)
     if op == "sum":
@@ -73,7 +75,29 @@ def call(L, op, x=P, rows=4, cols=8, eps=1e-6, plan=None, **kw):
     raise ValueError(op)
 
 
+def call_bf16(L, op, x, rows, cols, eps, plan, **kw):
+    if op == "rmsnorm":
+        return L.rmsnorm_bf16_ex(x, kw.get("w", P), kw.get("y", P), rows, cols, eps, plan, None)
+    if op == "sum":
+        return L.row_sum_bf16_ex(x, kw.get("out", P), rows, cols, plan, None)
+    if op == "softmax":
+        return L.softmax_bf16_ex(x, kw.get("y", P), rows, cols, plan, None)
+    if op == "layernorm":
+        return L.layernorm_bf16_ex(x, kw.get("gamma", P), kw.get("beta", P), kw.get("y", P), rows,
+                                   cols, eps, plan, None)
+    if op == "residual_layernorm":
+        return L.residual_layernorm_bf16_ex(x, kw.get("residual", P), kw.get("gamma", P),
+                                            kw.get("beta", P), kw.get("y", P), kw.get("h", None),
+                                            rows, cols, eps, plan, None)
+    if op == "cross_entropy":
+        return L.cross_entropy_bf16_ex(x, kw.get("targets", P), kw.get("loss", P), rows, cols, plan,
+                                       None)
+    raise ValueError(op)
+
+
 OPS = list(_capi.OP_IDS)
+MISALIGNED_BF16 = ctypes.c_void_p(0x10001)
+FLOAT_OUTS = {"sum": "out", "cross_entropy": "loss"}
 
 
 @pytest.mark.parametrize("op", OPS)
@@ -93,12 +117,17 @@ def test_bad_shapes(L, op):
 
 @pytest.mark.parametrize("op", OPS)
 def test_null_and_misaligned_pointers(L, op):
+    bf16 = op.endswith("_bf16")
+    base = op[:-5] if bf16 else op
+    bad = MISALIGNED_BF16 if bf16 else MISALIGNED
     assert call(L, op, x=NULL) == RR_ERR_INVALID_ARGUMENT
-    assert call(L, op, x=MISALIGNED) == RR_ERR_INVALID_ARGUMENT
+    assert call(L, op, x=bad) == RR_ERR_INVALID_ARGUMENT
     out_kw = {"rmsnorm": "y", "sum": "out", "softmax": "y", "layernorm": "y",
-              "residual_layernorm": "y", "cross_entropy": "loss"}[op]
+              "residual_layernorm": "y", "cross_entropy": "loss"}[base]
     assert call(L, op, **{out_kw: NULL}) == RR_ERR_INVALID_ARGUMENT
-    assert call(L, op, **{out_kw: MISALIGNED}) == RR_ERR_INVALID_ARGUMENT
+    # Float per-row outputs need 4-byte alignment even for bfloat16 inputs.
+    out_bad = MISALIGNED if (not bf16 or base in FLOAT_OUTS) else bad
+    assert call(L, op, **{out_kw: out_bad}) == RR_ERR_INVALID_ARGUMENT
 
 
 def test_operator_specific_pointers(L):
@@ -150,6 +179,30 @@ def test_illegal_plans_fail_closed(L, bad):
         assert call(L, op, rows=64, cols=4096, plan=bad) == RR_ERR_UNSUPPORTED
 
 
+def test_bf16_pack_width_rules(L):
+    rms16 = _capi.OP_IDS["rmsnorm_bf16"]
+    # V = 8 exists only for bfloat16 rows.
+    assert L.rr_check_plan(0, 64, 4096, plan(RR_PATH_ROW, 256, 256, 8, 16)) == RR_ERR_UNSUPPORTED
+    assert L.rr_check_plan(rms16, 64, 4096, plan(RR_PATH_ROW, 256, 256, 8, 16)) == RR_OK
+    # At most 32 live values per lane: 8 packs of 8 is over.
+    assert L.rr_check_plan(rms16, 64, 4096, plan(RR_PATH_ROW, 64, 64, 8, 64)) == RR_ERR_UNSUPPORTED
+    # V > 1 needs cols % V == 0 (naturally aligned packs).
+    assert L.rr_check_plan(rms16, 5, 257, plan(RR_PATH_ROW, 64, 64, 4, 8)) == RR_ERR_UNSUPPORTED
+    assert L.rr_check_plan(rms16, 5, 257, plan(RR_PATH_ROW, 64, 64, 1, 8)) == RR_OK
+    assert L.rr_check_plan(rms16, 5, 258, plan(RR_PATH_ROW, 64, 64, 2, 8)) == RR_OK
+    p = rr_plan()
+    assert L.rr_select_plan(rms16, 5, 257, p) == RR_OK and p.v == 1
+    assert L.rr_select_plan(rms16, 1024, 4096, p) == RR_OK and 4096 % p.v == 0
+
+
+def test_bf16_explicit_plan_needs_pointer_alignment(L):
+    """Pointers only 2-byte aligned cannot take 4-byte packs: refused, not remapped."""
+    p2 = ctypes.c_void_p(0x10002)
+    wide = plan(RR_PATH_ROW, 64, 64, 2, 2)
+    assert L.rmsnorm_bf16_ex(p2, P, P, 4, 128, 1e-6, wide, None) == RR_ERR_UNSUPPORTED
+    assert L.softmax_bf16_ex(P, p2, 4, 128, wide, None) == RR_ERR_UNSUPPORTED
+
+
 def test_v_wider_than_row_is_rejected(L):
     assert L.rr_check_plan(0, 1, 3, plan(RR_PATH_PACKED, 64, 8, 4, 4)) == RR_ERR_UNSUPPORTED
     assert L.rr_check_plan(0, 1, 3, plan(RR_PATH_PACKED, 64, 8, 2, 2)) == RR_OK
@@ -161,10 +214,10 @@ def test_check_plan_argument_errors(L):
     for cache in (0, 1, 2):
         good.cache = cache
         assert L.rr_check_plan(0, 64, 4096, good) == RR_OK
-    assert L.rr_check_plan(9, 64, 4096, good) == RR_ERR_INVALID_ARGUMENT
+    assert L.rr_check_plan(12, 64, 4096, good) == RR_ERR_INVALID_ARGUMENT
     assert L.rr_check_plan(0, 64, 0, good) == RR_ERR_INVALID_ARGUMENT
     assert L.rr_check_plan(0, 64, 4096, None) == RR_ERR_INVALID_ARGUMENT
-    assert L.rr_select_plan(9, 1, 1, rr_plan()) == RR_ERR_INVALID_ARGUMENT
+    assert L.rr_select_plan(12, 1, 1, rr_plan()) == RR_ERR_INVALID_ARGUMENT
     assert L.rr_select_plan(0, 1, 1, None) == RR_ERR_INVALID_ARGUMENT
 
 
