@@ -129,18 +129,19 @@ def shape_table(torch, rr, workloads, device, samples: int = 15) -> list:
     per call, host launch cost excluded); working sets of 1 MiB or more are
     also timed cold, cycling >= 768 MiB of distinct buffers. `single_call_us`
     is one synchronised host call, launch to completion. `copy_same_shape_*`
-    is rr_copy_f32 over a matrix of the same shape (8RC bytes) timed the same
-    way: the practical per-call bound at that size."""
+    is rr_copy_f32 over a matrix of the same shape and element size timed the
+    same way: the practical per-call bound at that size."""
     from row_reduction_amd.tune import COLD_BYTES, Case, GraphTimer, launches_per_graph
     out = []
     copy_cache = {}
 
-    def copy_ceiling(rows, cols, cold):
-        """Per-call us of rr_copy_f32 moving a rows x cols matrix (8RC bytes),
-        hot or cycling distinct buffers like the cold cases."""
-        key = (rows, cols, cold)
+    def copy_ceiling(rows, cols, cold, elem):
+        """Per-call us of rr_copy_f32 reading and writing a rows x cols matrix
+        of `elem`-byte elements (2 * elem * RC bytes), hot or cycling distinct
+        buffers like the cold cases."""
+        key = (rows, cols, cold, elem)
         if key not in copy_cache:
-            n = rows * cols
+            n = max(1, rows * cols * elem // 4)
             nsets = max(2, min(1024, COLD_BYTES // (8 * n))) if cold else 1
             src = [torch.randn(n, device=device) for _ in range(nsets)]
             dst = [torch.empty(n, device=device) for _ in range(nsets)]
@@ -156,12 +157,18 @@ def shape_table(torch, rr, workloads, device, samples: int = 15) -> list:
         return copy_cache[key]
     pairs = [("rmsnorm", s) for s in [(1, 127), (17, 257), (64, 4096), (1024, 4096)]]
     pairs += [(op, s) for s in workloads.FAMILY_SHAPES for op in workloads.OPS if op != "rmsnorm"]
+    pairs += [("rmsnorm_bf16", s) for s in [(1, 127), (17, 257), (64, 4096), (1024, 4096), (16384, 8192)]]
+    pairs += [(op + "_bf16", s) for s in workloads.FAMILY_SHAPES for op in workloads.OPS if op != "rmsnorm"]
     for op, (rows, cols) in pairs:
         plan = rr.rr_select_plan(op, rows, cols)
+        inherently_cold = False
         for hot in (True, False):
+            if not hot and inherently_cold:
+                break
             case = Case(torch, op, rows, cols, False, device, hot=hot)
             if not hot and not case.cold_possible:
                 continue
+            inherently_cold = hot and case.cold
             n = launches_per_graph(torch, case, plan)
             gt = GraphTimer(torch, case, plan, n)
             vals = sorted(gt.sample_us() for _ in range(samples))
@@ -177,7 +184,8 @@ def shape_table(torch, rr, workloads, device, samples: int = 15) -> list:
                 single.sort()
             nbytes = workloads.algorithmic_bytes(op, rows, cols)
             gbps = nbytes / (us * 1e3)
-            cus = copy_ceiling(rows, cols, case.cold)
+            elem = 2 if op.endswith("_bf16") else 4
+            cus = copy_ceiling(rows, cols, case.cold, elem)
             out.append({"op": op, "shape": f"{rows}x{cols}", "cache": "cold" if case.cold else "hot",
                         "us_per_op": round(us, 3), "min_us": round(vals[0], 3),
                         "max_us": round(vals[-1], 3), "launches_per_graph": n,
@@ -185,7 +193,7 @@ def shape_table(torch, rr, workloads, device, samples: int = 15) -> list:
                         "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
                         "single_call_us": round(single[len(single) // 2], 2) if single else None,
                         "copy_same_shape_us": round(cus, 3),
-                        "copy_same_shape_GBps": round(8 * rows * cols / (cus * 1e3), 1),
+                        "copy_same_shape_GBps": round(2 * elem * rows * cols / (cus * 1e3), 1),
                         "plan": plan.as_dict()})
             del gt, case
             torch.cuda.empty_cache()

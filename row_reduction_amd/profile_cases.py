@@ -38,6 +38,8 @@ def cases_list(shapes_only=None):
     from row_reduction_amd import workloads
     cases = [("rmsnorm", s) for s in [(1, 127), (17, 257), (64, 4096), (1024, 4096), (16384, 8192)]]
     cases += [(op, s) for s in workloads.FAMILY_SHAPES for op in workloads.OPS if op != "rmsnorm"]
+    cases += [("rmsnorm_bf16", s) for s in [(1024, 4096), (16384, 8192)]]
+    cases += [(op + "_bf16", (1024, 4096)) for op in workloads.OPS if op != "rmsnorm"]
     if shapes_only:
         cases = [c for c in cases if f"{c[1][0]}x{c[1][1]}" in shapes_only]
     return cases
@@ -122,7 +124,32 @@ def run(args) -> int:
 
 
 def ours(name: str) -> bool:
-    return "rowred::" in name or "copy_kernel" in name or "empty_kernel" in name
+    # The profiler leaves some names mangled (e.g. instances over __bf16).
+    return ("rowred::" in name or name.startswith("_ZN6rowred") or "copy_kernel" in name
+            or "empty_kernel" in name)
+
+
+def demangle(name: str) -> str:
+    """Readable name of a librowred kernel instance (template arguments in
+    order; bfloat16 shown as bf16), whether or not the trace demangled it."""
+    import re
+    if not name.startswith("_Z"):
+        return name
+    m = re.match(r"_ZN6rowred(\d+)(\w+?)I(.*)EEvNS_4ArgsE$", name)
+    if not m:
+        return name
+    kernel = m.group(2)[: int(m.group(1))]
+    args = []
+    for tok in re.findall(r"Li(-?\d+)E|Lb([01])E|(DF16b)|(f)(?=E|$)", m.group(3)):
+        if tok[0]:
+            args.append(tok[0])
+        elif tok[1]:
+            args.append("true" if tok[1] == "1" else "false")
+        elif tok[2]:
+            args.append("bf16")
+        else:
+            args.append("float")
+    return f"{kernel}<{', '.join(args)}>(Args)"
 
 
 def summarize(args) -> int:
@@ -152,7 +179,7 @@ def summarize(args) -> int:
     print("| Case | Kernel | Launches | Avg ns | Median ns | Min ns | Max ns | GB/s (median) | % of 8 TB/s |")
     print("|---|---|---:|---:|---:|---:|---:|---:|---:|")
     for e, kname, n, avg, med, lo, hi, gbps in out:
-        k = kname.replace("rowred::", "").replace("(rowred::Args)", "").replace("void ", "")
+        k = demangle(kname).replace("rowred::", "").replace("(rowred::Args)", "").replace("void ", "")
         k = k.replace("(anonymous namespace)::", "")
         g = f"{gbps:.1f}" if gbps else "—"
         f = f"{100 * gbps / PEAK_GBPS:.1f}" if gbps else "—"

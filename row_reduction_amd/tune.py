@@ -42,6 +42,8 @@ ROOT = os.path.dirname(HERE)
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+import numpy as np  # noqa: E402
+
 from row_reduction_amd import _capi, plans, workloads  # noqa: E402
 from row_reduction_amd._capi import rr_plan  # noqa: E402
 
@@ -66,7 +68,12 @@ def source_hash() -> str:
 
 
 def host_inputs(op: str, rows: int, cols: int, held_out: bool) -> dict:
-    """Seeded inputs with the measured configurations' distributions."""
+    """Seeded inputs with the measured configurations' distributions (bfloat16
+    operators: the same draws as bfloat16 bit patterns)."""
+    if op.endswith("_bf16"):
+        d = host_inputs(op[:-5], rows, cols, held_out)
+        return {k: (workloads.as_bf16_bits(v) if isinstance(v, np.ndarray) and v.dtype == np.float32
+                    else v) for k, v in d.items()}
     if op == "rmsnorm":
         k = {(1, 127): 1, (17, 257): 2, (64, 4096): 3}.get((rows, cols), 4)
         seed = (2000 if held_out else 1000) + k
@@ -86,20 +93,31 @@ class Case:
         self.torch, self.rr, self.op, self.rows, self.cols = torch, rr, op, rows, cols
         h = host_inputs(op, rows, cols, held_out)
         self.eps = h["eps"]
-        dev = {k: torch.from_numpy(v).to(device) for k, v in h.items() if k != "eps"}
-        per_set = 4 * rows * cols * (3 if op == "residual_layernorm" else 2)
+        self.bf16 = op.endswith("_bf16")
+        self.base = op[:-5] if self.bf16 else op
+
+        def dev_tensor(v):
+            if v.dtype == np.uint16:
+                return torch.from_numpy(v.view(np.int16)).to(device).view(torch.bfloat16)
+            return torch.from_numpy(v).to(device)
+        dev = {k: dev_tensor(v) for k, v in h.items() if k != "eps"}
+        elem = 2 if self.bf16 else 4
+        per_set = elem * rows * cols * (3 if self.base == "residual_layernorm" else 2)
+        # Cold: enough distinct sets that the cycled footprint is >= COLD_BYTES,
+        # three times the 256 MB last-level cache, so no launch finds its data
+        # there. A single set of COLD_BYTES or more is cold by itself.
         self.nsets = 1
-        if not hot and per_set * 8 < COLD_BYTES and per_set >= (1 << 20):
-            self.nsets = int(min(1024, max(2, COLD_BYTES // per_set)))
-        self.cold = self.nsets > 1 or per_set * 8 >= COLD_BYTES
+        if not hot and per_set >= (1 << 20):
+            self.nsets = int(min(1024, -(-COLD_BYTES // per_set)))
+        self.cold = self.nsets > 1 or per_set >= COLD_BYTES
         self.cold_possible = per_set >= (1 << 20)
         self.sets = []
         for _ in range(self.nsets):
             s = dict(dev)
             s["x"] = dev["x"].clone()
-            if op == "residual_layernorm":
+            if self.base == "residual_layernorm":
                 s["residual"] = dev["residual"].clone()
-            if op in ("sum", "cross_entropy"):
+            if self.base in ("sum", "cross_entropy"):
                 s["out"] = torch.empty(rows, dtype=torch.float32, device=device)
             else:
                 s["out"] = torch.empty_like(dev["x"])
@@ -107,20 +125,20 @@ class Case:
 
     def launch(self, i: int, plan) -> None:
         s, rr = self.sets[i % self.nsets], self.rr
-        op = self.op
+        op, sfx = self.base, ("_bf16" if self.bf16 else "_f32")
         if op == "rmsnorm":
-            rr.rmsnorm_f32(s["x"], s["w"], self.eps, y=s["out"], plan=plan)
+            getattr(rr, "rmsnorm" + sfx)(s["x"], s["w"], self.eps, y=s["out"], plan=plan)
         elif op == "sum":
-            rr.row_sum_f32(s["x"], out=s["out"], plan=plan)
+            getattr(rr, "row_sum" + sfx)(s["x"], out=s["out"], plan=plan)
         elif op == "softmax":
-            rr.softmax_f32(s["x"], y=s["out"], plan=plan)
+            getattr(rr, "softmax" + sfx)(s["x"], y=s["out"], plan=plan)
         elif op == "layernorm":
-            rr.layernorm_f32(s["x"], s["w"], s["beta"], self.eps, y=s["out"], plan=plan)
+            getattr(rr, "layernorm" + sfx)(s["x"], s["w"], s["beta"], self.eps, y=s["out"], plan=plan)
         elif op == "residual_layernorm":
-            rr.residual_layernorm_f32(s["x"], s["residual"], s["w"], s["beta"], self.eps,
-                                      y=s["out"], plan=plan)
+            getattr(rr, "residual_layernorm" + sfx)(s["x"], s["residual"], s["w"], s["beta"], self.eps,
+                                                    y=s["out"], plan=plan)
         elif op == "cross_entropy":
-            rr.cross_entropy_f32(s["x"], s["targets"], loss=s["out"], plan=plan)
+            getattr(rr, "cross_entropy" + sfx)(s["x"], s["targets"], loss=s["out"], plan=plan)
 
     def output(self):
         return self.sets[0]["out"]
@@ -170,10 +188,12 @@ def launches_per_graph(torch, case: Case, plan) -> int:
 
 
 def close(a, b) -> bool:
-    import numpy as np
+    """Outputs of two plans agree: float within 2e-5 relative, bfloat16 within
+    one unit in the last place (2^-7 relative)."""
+    rel = 2.0 ** -7 if a.dtype != b.dtype or str(a.dtype) == "torch.bfloat16" else 2e-5
     a = a.double().cpu().numpy()
     b = b.double().cpu().numpy()
-    return bool(np.all(np.abs(a - b) <= 2e-5 + 2e-5 * np.abs(b)))
+    return bool(np.all(np.abs(a - b) <= 2e-5 + rel * np.abs(b)))
 
 
 def measure(torch, case: Case, candidates: dict, rounds: int, samples: int) -> dict:
@@ -288,8 +308,9 @@ def emit_table(path: str) -> str:
     lines = ["// Measured per-shape plans: {op, rows, cols, {path, block, lanes_per_row, rows_per_group, v, slots, cache}},",
              "// generated by row_reduction_amd/tune.py: the fastest legal plan of a GPU search on",
              "// MI355X, re-measured against the incumbent plan on held-out inputs in a",
-             f"// fresh process (device source sha256 {rep['source_sha256']}).",
-             "// Every measured shape is listed, so the table does not depend on the built-in rule."]
+             "// fresh process. [xxxxxxxx] on each line is the start of the sha256 of the device",
+             "// sources it was measured under. Every measured shape is listed, so the table does",
+             "// not depend on the built-in rule."]
     for c in rep["cases"]:
         # An unconfirmed winner leaves the incumbent (the plan selected when
         # the search ran) in place: the replay showed it at least as fast.
@@ -301,10 +322,22 @@ def emit_table(path: str) -> str:
         lines.append(f"{{{_capi.OP_IDS[c['op']]}, {c['rows']}, {c['cols']}, {{{p['path']}, {p['block']}, "
                      f"{p['lanes_per_row']}, {p['rows_per_group']}, {p['v']}, {p['slots']}, "
                      f"{p.get('cache', 0)}}}}},  "
-                     f"// {c['op']} {c['rows']}x{c['cols']}: {r['us']:.3f} us"
+                     f"// [{rep['source_sha256'][:8]}] {c['op']} {c['rows']}x{c['cols']}: {r['us']:.3f} us"
                      + (f", x{c.get('paired_speedup_median', 1.0):.3f} vs incumbent" if c.get("confirmed")
                         else ", incumbent kept"))
+    # Entries of the existing table for (op, rows, cols) this replay did not
+    # measure are kept, with the device-source hash they were measured under.
     target = os.path.join(HERE, "csrc", "plan_table.inc")
+    measured = {(_capi.OP_IDS[c["op"]], c["rows"], c["cols"]) for c in rep["cases"]}
+    kept = []
+    if os.path.exists(target):
+        for line in open(target):
+            if line.startswith("{"):
+                head = line[1:].split(",")
+                key = (int(head[0]), int(head[1]), int(head[2]))
+                if key not in measured:
+                    kept.append(line.rstrip("\n"))
+    lines += kept
     with open(target, "w") as f:
         f.write("\n".join(lines) + "\n")
     return target
@@ -337,7 +370,7 @@ def summarize(search_path: str, replay_path: str) -> str:
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--ops", default=",".join(workloads.OPS))
+    ap.add_argument("--ops", default=",".join(list(workloads.OPS) + [o + "_bf16" for o in workloads.OPS]))
     ap.add_argument("--shapes", default=",".join(DEFAULT_SHAPES))
     ap.add_argument("--rounds", type=int, default=2)
     ap.add_argument("--samples", type=int, default=5)
