@@ -209,6 +209,38 @@ def host_cores() -> int:
     return max(1, min(16, n))
 
 
+def long_rows_table(torch, rr, device, samples: int = 11) -> list:
+    """Few long rows: the plan the plain entry points use (one workgroup per
+    row, register or streaming path) against the split-row plan the *_ws
+    entry points select with a workspace, per call (graph-replayed), hot and
+    cycling distinct buffers."""
+    from row_reduction_amd import workloads
+    from row_reduction_amd.tune import Case, GraphTimer, launches_per_graph
+    out = []
+    shapes = [(1, 1 << 20), (8, 1 << 18), (32, 65536)]
+    for op in ("rmsnorm", "softmax", "row_sum", "rmsnorm_bf16"):
+        opn = "sum" if op == "row_sum" else op
+        for rows, cols in shapes:
+            rec = {"op": opn, "shape": f"{rows}x{cols}"}
+            for mode, ws in (("plain", False), ("split", True)):
+                case = Case(torch, opn, rows, cols, False, device, hot=False, workspace=ws)
+                plan = None
+                n = launches_per_graph(torch, case, plan)
+                gt = GraphTimer(torch, case, plan, n)
+                vals = sorted(gt.sample_us() for _ in range(samples))
+                us = vals[len(vals) // 2]
+                nbytes = workloads.algorithmic_bytes(opn, rows, cols)
+                chosen = rr.rr_select_plan(opn, rows, cols).as_dict() if not ws else None
+                rec[mode] = {"us_per_op": round(us, 3), "GBps": round(nbytes / (us * 1e3), 1),
+                             "cache": "cold" if case.cold else "hot",
+                             "plan": chosen if chosen else "split (selected with workspace)"}
+                del gt, case
+                torch.cuda.empty_cache()
+            rec["split_speedup"] = round(rec["plain"]["us_per_op"] / rec["split"]["us_per_op"], 3)
+            out.append(rec)
+    return out
+
+
 def cpu_baseline(workloads, x_np, w_np, eps, y_gpu_sample, budget_s: float = 10.0) -> dict:
     """The CPU oracle, as it is (plain fp64 C loops), on row blocks of the
     headline input: first on one thread, then on every host core with a
@@ -332,6 +364,7 @@ def main() -> int:
         torch.cuda.synchronize()
         y_sample = y[:256].cpu().numpy()
     shapes = [] if args.no_shapes else shape_table(torch, rr, workloads, device)
+    long_rows = [] if args.no_shapes else long_rows_table(torch, rr, device)
 
     result = {
         "metric": METRIC,
@@ -357,6 +390,7 @@ def main() -> int:
                          "GBps": round(copy_gbps, 1), "frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4)},
         "launch_floor_us": round(empty["us"], 3),
         "shapes": shapes,
+        "long_rows": long_rows,
     }
     if not args.no_cpu:
         log(f"cpu baseline ({args.cpu_seconds:.0f} s)")

@@ -82,11 +82,21 @@ typedef enum rr_op {
  *                   wavefronts (combined through LDS with one barrier per
  *                   reduction); a workgroup may hold several rows.
  *   RR_PATH_LOOP:   one row per workgroup, values are re-read from memory
- *                   instead of kept in registers; any cols. */
+ *                   instead of kept in registers; any cols.
+ *   RR_PATH_SPLIT:  a row is cut into S = ceil(cols / (lanes_per_row * slots))
+ *                   slices, one workgroup each (2 <= S <= 1024, rows <= 65535):
+ *                   a first launch keeps each slice in registers and writes
+ *                   one 16-byte partial per (row, slice) to a caller-provided
+ *                   workspace, a second merges the partials in slice order
+ *                   and writes the outputs (re-reading the slice for the
+ *                   per-element operators). Only through the *_ws entry
+ *                   points; v = 4 (float) or 8 (bfloat16, cols % 8 == 0),
+ *                   slots 16 or 32, cache 2. */
 typedef enum rr_path {
     RR_PATH_PACKED = 0,
     RR_PATH_ROW = 1,
-    RR_PATH_LOOP = 2
+    RR_PATH_LOOP = 2,
+    RR_PATH_SPLIT = 3
 } rr_path;
 
 /* A launch plan. Worker w (0 <= w < lanes_per_row) of a row owns logical
@@ -214,6 +224,55 @@ int residual_layernorm_bf16_ex(const uint16_t *x, const uint16_t *residual,
                                const rr_plan *plan, void *stream);
 int cross_entropy_bf16_ex(const uint16_t *logits, const int32_t *targets, float *loss,
                           int64_t rows, int64_t cols, const rr_plan *plan, void *stream);
+
+/* ---- split rows with a caller workspace --------------------------------------
+ * The *_ws forms take, besides an optional explicit plan, a device workspace
+ * of workspace_bytes bytes (16-byte aligned, caller-owned; its contents need
+ * no initialisation and are scratch between the two launches of a split
+ * plan). With plan == NULL the selector may then pick RR_PATH_SPLIT for
+ * shapes with few, long rows when workspace_bytes suffices, else it picks as
+ * the plain forms do; an explicit split plan with too small a workspace
+ * returns RR_ERR_UNSUPPORTED. Calls that share one workspace on different
+ * streams race. rr_workspace_bytes gives the size a plan needs (the selected
+ * one when plan == NULL): rows * S * 16 for a split plan, 0 otherwise, or
+ * -1 for invalid arguments. These entry points exist for long rows that
+ * leave most compute units idle on the one-workgroup-per-row paths (the
+ * spreading of one long row across workers that the LuisaCompute page's
+ * "Evidence and what remains" section names as next work). */
+int64_t rr_workspace_bytes(int op, int64_t rows, int64_t cols, const rr_plan *plan);
+int rmsnorm_f32_ws(const float *x, const float *w, float *y, int64_t rows, int64_t cols, float eps,
+                   const rr_plan *plan, void *workspace, int64_t workspace_bytes, void *stream);
+int row_sum_f32_ws(const float *x, float *out, int64_t rows, int64_t cols,
+                   const rr_plan *plan, void *workspace, int64_t workspace_bytes, void *stream);
+int softmax_f32_ws(const float *x, float *y, int64_t rows, int64_t cols,
+                   const rr_plan *plan, void *workspace, int64_t workspace_bytes, void *stream);
+int layernorm_f32_ws(const float *x, const float *gamma, const float *beta, float *y,
+                     int64_t rows, int64_t cols, float eps,
+                     const rr_plan *plan, void *workspace, int64_t workspace_bytes, void *stream);
+int residual_layernorm_f32_ws(const float *x, const float *residual, const float *gamma,
+                              const float *beta, float *y, float *h_out, int64_t rows, int64_t cols,
+                              float eps, const rr_plan *plan, void *workspace,
+                              int64_t workspace_bytes, void *stream);
+int cross_entropy_f32_ws(const float *logits, const int32_t *targets, float *loss,
+                         int64_t rows, int64_t cols,
+                         const rr_plan *plan, void *workspace, int64_t workspace_bytes, void *stream);
+int rmsnorm_bf16_ws(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t rows, int64_t cols,
+                    float eps, const rr_plan *plan, void *workspace, int64_t workspace_bytes,
+                    void *stream);
+int row_sum_bf16_ws(const uint16_t *x, float *out, int64_t rows, int64_t cols,
+                    const rr_plan *plan, void *workspace, int64_t workspace_bytes, void *stream);
+int softmax_bf16_ws(const uint16_t *x, uint16_t *y, int64_t rows, int64_t cols,
+                    const rr_plan *plan, void *workspace, int64_t workspace_bytes, void *stream);
+int layernorm_bf16_ws(const uint16_t *x, const uint16_t *gamma, const uint16_t *beta, uint16_t *y,
+                      int64_t rows, int64_t cols, float eps,
+                      const rr_plan *plan, void *workspace, int64_t workspace_bytes, void *stream);
+int residual_layernorm_bf16_ws(const uint16_t *x, const uint16_t *residual, const uint16_t *gamma,
+                               const uint16_t *beta, uint16_t *y, uint16_t *h_out, int64_t rows,
+                               int64_t cols, float eps, const rr_plan *plan, void *workspace,
+                               int64_t workspace_bytes, void *stream);
+int cross_entropy_bf16_ws(const uint16_t *logits, const int32_t *targets, float *loss,
+                          int64_t rows, int64_t cols,
+                          const rr_plan *plan, void *workspace, int64_t workspace_bytes, void *stream);
 
 /* Plan the library would use for (op, rows, cols): the measured per-shape
  * table entry when one exists, else the built-in rule. Pure host function;

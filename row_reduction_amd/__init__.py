@@ -21,6 +21,7 @@ __all__ = [
     "rmsnorm_bf16", "row_sum_bf16", "softmax_bf16", "layernorm_bf16",
     "residual_layernorm_bf16", "cross_entropy_bf16",
     "rr_select_plan", "rr_check_plan", "rr_status_string", "rr_copy_f32", "rr_empty_kernel",
+    "rr_workspace_bytes", "workspace_for",
     "rr_plan", "RowRedError", "OP_IDS",
 ]
 
@@ -72,6 +73,26 @@ def _out_rows(out, x, name):
     return _vec(out, x.shape[0], name)
 
 
+def _ws(workspace):
+    """(pointer, bytes) of an optional workspace tensor (any dtype, on the GPU)."""
+    if workspace is None:
+        return None, 0
+    torch = _torch()
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous CUDA/HIP tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def workspace_for(op, rows, cols, plan=None, device=None):
+    """A workspace tensor large enough for `op` on (rows, cols) with `plan`
+    (the selector's choice when None), or None when the plan needs none."""
+    n = rr_workspace_bytes(op, rows, cols, plan)
+    if n <= 0:
+        return None
+    torch = _torch()
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
 def _plan_ptr(plan):
     if plan is None:
         return None
@@ -80,55 +101,55 @@ def _plan_ptr(plan):
     return plan
 
 
-def rmsnorm_f32(x, w, eps=1e-6, y=None, plan=None, stream=None):
+def rmsnorm_f32(x, w, eps=1e-6, y=None, plan=None, workspace=None, stream=None):
     """y[r,c] = x[r,c] * w[c] / sqrt(mean_c x[r,c]^2 + eps). Returns y."""
     _mat(x, "x")
     rows, cols = x.shape
     _vec(w, cols, "w")
     y = _out_like(y, x, "y")
-    st = _capi.lib().rmsnorm_f32_ex(x.data_ptr(), w.data_ptr(), y.data_ptr(), rows, cols, float(eps),
-                                     _plan_ptr(plan), _stream(stream))
+    st = _capi.lib().rmsnorm_f32_ws(x.data_ptr(), w.data_ptr(), y.data_ptr(), rows, cols, float(eps),
+                                     _plan_ptr(plan), *_ws(workspace), _stream(stream))
     _capi.check("rmsnorm_f32", st)
     return y
 
 
-def row_sum_f32(x, out=None, plan=None, stream=None):
+def row_sum_f32(x, out=None, plan=None, workspace=None, stream=None):
     """out[r] = sum_c x[r,c] (float64 accumulation, one rounding). Returns out."""
     _mat(x, "x")
     rows, cols = x.shape
     out = _out_rows(out, x, "out")
-    st = _capi.lib().row_sum_f32_ex(x.data_ptr(), out.data_ptr(), rows, cols, _plan_ptr(plan),
-                                     _stream(stream))
+    st = _capi.lib().row_sum_f32_ws(x.data_ptr(), out.data_ptr(), rows, cols, _plan_ptr(plan),
+                                     *_ws(workspace), _stream(stream))
     _capi.check("row_sum_f32", st)
     return out
 
 
-def softmax_f32(x, y=None, plan=None, stream=None):
+def softmax_f32(x, y=None, plan=None, workspace=None, stream=None):
     """Row softmax with the row maximum subtracted. Returns y."""
     _mat(x, "x")
     rows, cols = x.shape
     y = _out_like(y, x, "y")
-    st = _capi.lib().softmax_f32_ex(x.data_ptr(), y.data_ptr(), rows, cols, _plan_ptr(plan),
-                                     _stream(stream))
+    st = _capi.lib().softmax_f32_ws(x.data_ptr(), y.data_ptr(), rows, cols, _plan_ptr(plan),
+                                     *_ws(workspace), _stream(stream))
     _capi.check("softmax_f32", st)
     return y
 
 
-def layernorm_f32(x, gamma, beta, eps=1e-5, y=None, plan=None, stream=None):
+def layernorm_f32(x, gamma, beta, eps=1e-5, y=None, plan=None, workspace=None, stream=None):
     """y = (x - mean) / sqrt(var + eps) * gamma + beta per row. Returns y."""
     _mat(x, "x")
     rows, cols = x.shape
     _vec(gamma, cols, "gamma")
     _vec(beta, cols, "beta")
     y = _out_like(y, x, "y")
-    st = _capi.lib().layernorm_f32_ex(x.data_ptr(), gamma.data_ptr(), beta.data_ptr(), y.data_ptr(),
-                                       rows, cols, float(eps), _plan_ptr(plan), _stream(stream))
+    st = _capi.lib().layernorm_f32_ws(x.data_ptr(), gamma.data_ptr(), beta.data_ptr(), y.data_ptr(),
+                                       rows, cols, float(eps), _plan_ptr(plan), *_ws(workspace), _stream(stream))
     _capi.check("layernorm_f32", st)
     return y
 
 
 def residual_layernorm_f32(x, residual, gamma, beta, eps=1e-5, y=None, h_out=None, plan=None,
-                           stream=None):
+                           workspace=None, stream=None):
     """h = x + residual (float32); y = LayerNorm(h). Writes h to h_out when given. Returns y."""
     _mat(x, "x")
     rows, cols = x.shape
@@ -142,22 +163,22 @@ def residual_layernorm_f32(x, residual, gamma, beta, eps=1e-5, y=None, h_out=Non
     if h_out is not None:
         _out_like(h_out, x, "h_out")
         h_ptr = h_out.data_ptr()
-    st = _capi.lib().residual_layernorm_f32_ex(x.data_ptr(), residual.data_ptr(), gamma.data_ptr(),
+    st = _capi.lib().residual_layernorm_f32_ws(x.data_ptr(), residual.data_ptr(), gamma.data_ptr(),
                                                 beta.data_ptr(), y.data_ptr(), h_ptr, rows, cols,
-                                                float(eps), _plan_ptr(plan), _stream(stream))
+                                                float(eps), _plan_ptr(plan), *_ws(workspace), _stream(stream))
     _capi.check("residual_layernorm_f32", st)
     return y
 
 
-def cross_entropy_f32(logits, targets, loss=None, plan=None, stream=None):
+def cross_entropy_f32(logits, targets, loss=None, plan=None, workspace=None, stream=None):
     """loss[r] = logsumexp_c logits[r,c] - logits[r, targets[r]]. Returns loss."""
     torch = _torch()
     _mat(logits, "logits")
     rows, cols = logits.shape
     _vec(targets, rows, "targets", dtype=torch.int32)
     loss = _out_rows(loss, logits, "loss")
-    st = _capi.lib().cross_entropy_f32_ex(logits.data_ptr(), targets.data_ptr(), loss.data_ptr(),
-                                           rows, cols, _plan_ptr(plan), _stream(stream))
+    st = _capi.lib().cross_entropy_f32_ws(logits.data_ptr(), targets.data_ptr(), loss.data_ptr(),
+                                           rows, cols, _plan_ptr(plan), *_ws(workspace), _stream(stream))
     _capi.check("cross_entropy_f32", st)
     return loss
 
@@ -168,55 +189,55 @@ def _bf16():
     return _torch().bfloat16
 
 
-def rmsnorm_bf16(x, w, eps=1e-6, y=None, plan=None, stream=None):
+def rmsnorm_bf16(x, w, eps=1e-6, y=None, plan=None, workspace=None, stream=None):
     """rmsnorm_f32 on bfloat16 x, w, y. Returns y."""
     _mat(x, "x", _bf16())
     rows, cols = x.shape
     _vec(w, cols, "w", _bf16())
     y = _out_like(y, x, "y")
-    st = _capi.lib().rmsnorm_bf16_ex(x.data_ptr(), w.data_ptr(), y.data_ptr(), rows, cols, float(eps),
-                                      _plan_ptr(plan), _stream(stream))
+    st = _capi.lib().rmsnorm_bf16_ws(x.data_ptr(), w.data_ptr(), y.data_ptr(), rows, cols, float(eps),
+                                      _plan_ptr(plan), *_ws(workspace), _stream(stream))
     _capi.check("rmsnorm_bf16", st)
     return y
 
 
-def row_sum_bf16(x, out=None, plan=None, stream=None):
+def row_sum_bf16(x, out=None, plan=None, workspace=None, stream=None):
     """Row sums of bfloat16 x as float32 (float64 accumulation). Returns out."""
     _mat(x, "x", _bf16())
     rows, cols = x.shape
     out = _out_rows(out, x, "out")
-    st = _capi.lib().row_sum_bf16_ex(x.data_ptr(), out.data_ptr(), rows, cols, _plan_ptr(plan),
-                                      _stream(stream))
+    st = _capi.lib().row_sum_bf16_ws(x.data_ptr(), out.data_ptr(), rows, cols, _plan_ptr(plan),
+                                      *_ws(workspace), _stream(stream))
     _capi.check("row_sum_bf16", st)
     return out
 
 
-def softmax_bf16(x, y=None, plan=None, stream=None):
+def softmax_bf16(x, y=None, plan=None, workspace=None, stream=None):
     """softmax_f32 on bfloat16 x, y. Returns y."""
     _mat(x, "x", _bf16())
     rows, cols = x.shape
     y = _out_like(y, x, "y")
-    st = _capi.lib().softmax_bf16_ex(x.data_ptr(), y.data_ptr(), rows, cols, _plan_ptr(plan),
-                                      _stream(stream))
+    st = _capi.lib().softmax_bf16_ws(x.data_ptr(), y.data_ptr(), rows, cols, _plan_ptr(plan),
+                                      *_ws(workspace), _stream(stream))
     _capi.check("softmax_bf16", st)
     return y
 
 
-def layernorm_bf16(x, gamma, beta, eps=1e-5, y=None, plan=None, stream=None):
+def layernorm_bf16(x, gamma, beta, eps=1e-5, y=None, plan=None, workspace=None, stream=None):
     """layernorm_f32 on bfloat16 x, gamma, beta, y. Returns y."""
     _mat(x, "x", _bf16())
     rows, cols = x.shape
     _vec(gamma, cols, "gamma", _bf16())
     _vec(beta, cols, "beta", _bf16())
     y = _out_like(y, x, "y")
-    st = _capi.lib().layernorm_bf16_ex(x.data_ptr(), gamma.data_ptr(), beta.data_ptr(), y.data_ptr(),
-                                        rows, cols, float(eps), _plan_ptr(plan), _stream(stream))
+    st = _capi.lib().layernorm_bf16_ws(x.data_ptr(), gamma.data_ptr(), beta.data_ptr(), y.data_ptr(),
+                                        rows, cols, float(eps), _plan_ptr(plan), *_ws(workspace), _stream(stream))
     _capi.check("layernorm_bf16", st)
     return y
 
 
 def residual_layernorm_bf16(x, residual, gamma, beta, eps=1e-5, y=None, h_out=None, plan=None,
-                            stream=None):
+                            workspace=None, stream=None):
     """h = bf16(x + residual); y = LayerNorm(h), bfloat16 storage. Returns y."""
     _mat(x, "x", _bf16())
     rows, cols = x.shape
@@ -230,24 +251,34 @@ def residual_layernorm_bf16(x, residual, gamma, beta, eps=1e-5, y=None, h_out=No
     if h_out is not None:
         _out_like(h_out, x, "h_out")
         h_ptr = h_out.data_ptr()
-    st = _capi.lib().residual_layernorm_bf16_ex(x.data_ptr(), residual.data_ptr(), gamma.data_ptr(),
+    st = _capi.lib().residual_layernorm_bf16_ws(x.data_ptr(), residual.data_ptr(), gamma.data_ptr(),
                                                  beta.data_ptr(), y.data_ptr(), h_ptr, rows, cols,
-                                                 float(eps), _plan_ptr(plan), _stream(stream))
+                                                 float(eps), _plan_ptr(plan), *_ws(workspace), _stream(stream))
     _capi.check("residual_layernorm_bf16", st)
     return y
 
 
-def cross_entropy_bf16(logits, targets, loss=None, plan=None, stream=None):
+def cross_entropy_bf16(logits, targets, loss=None, plan=None, workspace=None, stream=None):
     """cross_entropy_f32 on bfloat16 logits; float32 loss. Returns loss."""
     torch = _torch()
     _mat(logits, "logits", _bf16())
     rows, cols = logits.shape
     _vec(targets, rows, "targets", dtype=torch.int32)
     loss = _out_rows(loss, logits, "loss")
-    st = _capi.lib().cross_entropy_bf16_ex(logits.data_ptr(), targets.data_ptr(), loss.data_ptr(),
-                                            rows, cols, _plan_ptr(plan), _stream(stream))
+    st = _capi.lib().cross_entropy_bf16_ws(logits.data_ptr(), targets.data_ptr(), loss.data_ptr(),
+                                            rows, cols, _plan_ptr(plan), *_ws(workspace), _stream(stream))
     _capi.check("cross_entropy_bf16", st)
     return loss
+
+
+def rr_workspace_bytes(op, rows, cols, plan=None) -> int:
+    """Workspace bytes `plan` needs on (rows, cols) (the selected plan when
+    None, given unlimited workspace); 0 when it needs none."""
+    op_id = OP_IDS[op] if isinstance(op, str) else int(op)
+    n = _capi.lib().rr_workspace_bytes(op_id, rows, cols, _plan_ptr(plan))
+    if n < 0:
+        raise RowRedError("rr_workspace_bytes", _capi.RR_ERR_INVALID_ARGUMENT)
+    return n
 
 
 def rr_select_plan(op, rows, cols) -> rr_plan:

@@ -29,6 +29,7 @@ RR_OP_BF16_OFFSET = 6   # RR_OP_<op>_BF16 = RR_OP_<op> + 6
 RR_PATH_PACKED = 0
 RR_PATH_ROW = 1
 RR_PATH_LOOP = 2
+RR_PATH_SPLIT = 3
 
 OP_IDS = {
     "rmsnorm": RR_OP_RMSNORM,
@@ -50,6 +51,11 @@ EXPORTED = (
     "residual_layernorm_bf16", "cross_entropy_bf16",
     "rmsnorm_bf16_ex", "row_sum_bf16_ex", "softmax_bf16_ex", "layernorm_bf16_ex",
     "residual_layernorm_bf16_ex", "cross_entropy_bf16_ex",
+    "rmsnorm_f32_ws", "row_sum_f32_ws", "softmax_f32_ws", "layernorm_f32_ws",
+    "residual_layernorm_f32_ws", "cross_entropy_f32_ws",
+    "rmsnorm_bf16_ws", "row_sum_bf16_ws", "softmax_bf16_ws", "layernorm_bf16_ws",
+    "residual_layernorm_bf16_ws", "cross_entropy_bf16_ws",
+    "rr_workspace_bytes",
     "rr_select_plan", "rr_check_plan", "rr_status_string",
     "rr_copy_f32", "rr_empty_kernel",
 )
@@ -107,6 +113,19 @@ _SIGNATURES = {
     "layernorm_bf16_ex": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp],
     "residual_layernorm_bf16_ex": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp],
     "cross_entropy_bf16_ex": [_vp, _vp, _vp, _i64, _i64, _planp, _vp],
+    "rmsnorm_f32_ws": [_vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp, _i64, _vp],
+    "row_sum_f32_ws": [_vp, _vp, _i64, _i64, _planp, _vp, _i64, _vp],
+    "softmax_f32_ws": [_vp, _vp, _i64, _i64, _planp, _vp, _i64, _vp],
+    "layernorm_f32_ws": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp, _i64, _vp],
+    "residual_layernorm_f32_ws": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp, _i64, _vp],
+    "cross_entropy_f32_ws": [_vp, _vp, _vp, _i64, _i64, _planp, _vp, _i64, _vp],
+    "rmsnorm_bf16_ws": [_vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp, _i64, _vp],
+    "row_sum_bf16_ws": [_vp, _vp, _i64, _i64, _planp, _vp, _i64, _vp],
+    "softmax_bf16_ws": [_vp, _vp, _i64, _i64, _planp, _vp, _i64, _vp],
+    "layernorm_bf16_ws": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp, _i64, _vp],
+    "residual_layernorm_bf16_ws": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp, _i64, _vp],
+    "cross_entropy_bf16_ws": [_vp, _vp, _vp, _i64, _i64, _planp, _vp, _i64, _vp],
+    "rr_workspace_bytes": [ctypes.c_int, _i64, _i64, _planp],
     "rr_select_plan": [ctypes.c_int, _i64, _i64, _planp],
     "rr_check_plan": [ctypes.c_int, _i64, _i64, _planp],
     "rr_status_string": [ctypes.c_int],
@@ -129,7 +148,8 @@ def lib() -> ctypes.CDLL:
         for name, argtypes in _SIGNATURES.items():
             fn = getattr(L, name)
             fn.argtypes = argtypes
-            fn.restype = ctypes.c_char_p if name == "rr_status_string" else ctypes.c_int
+            fn.restype = {"rr_status_string": ctypes.c_char_p,
+                          "rr_workspace_bytes": ctypes.c_int64}.get(name, ctypes.c_int)
         _lib = L
     return _lib
 

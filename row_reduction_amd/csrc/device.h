@@ -258,6 +258,7 @@ struct AddOp {
 };
 struct MaxOp {
     __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+    __device__ __forceinline__ double operator()(double a, double b) const { return fmax(a, b); }
 };
 
 // Balanced tree over K (a power of two) values; overwrites t.
@@ -672,6 +673,231 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
     }
 }
 
+// ---- split rows: several workgroups per row ---------------------------------------
+//
+// For rows longer than one workgroup's register budget when there are too few
+// rows to fill the chip. Row r is cut into S slices of W*K columns; workgroup
+// (s, r) keeps slice s in registers (same ownership map inside the slice) and
+// writes one partial per (row, slice) to the caller's workspace; a second
+// launch merges the row's S partials in slice order (float64), re-reads its
+// slice and writes the outputs. Partials:
+//   RMSNorm: (sum x^2, -)          row sum: (sum x, -)
+//   softmax / cross-entropy: (slice max m, sum exp(x - m))
+//   LayerNorm: (slice mean, slice sum of squared deviations), merged with
+//   Chan's pairwise formula so no sum of squares of raw values is formed.
+
+struct Partial2 {
+    double a, b;
+};
+
+// Columns of slice s: [s * span, min((s + 1) * span, cols)).
+__device__ __forceinline__ int slice_len(int s, int span, int cols) {
+    const int left = cols - s * span;
+    return left < span ? left : span;
+}
+
+template <int OP, int V, int NCHUNK, int HINT, class T>
+__global__ void __launch_bounds__(1024) split_partial_kernel(const Args a) {
+    constexpr int K = V * NCHUNK;
+    __shared__ float lds0[16];
+    __shared__ float lds1[16];
+    __shared__ double ldsd[16];
+    const RowLanes<64> rl(a);
+    const int cols = a.cols;
+    const int s = blockIdx.x;
+    const int64_t row = blockIdx.y;
+    const int64_t off = row * (int64_t)cols;
+    const int span = rl.W * K;
+    const int first = s * span;
+    const int stride = rl.W * V;
+    const int base = first + rl.lane * V;
+    const T *xr = static_cast<const T *>(a.x) + off;
+    constexpr bool kMaxFirst = (OP == kSoftmax || OP == kCrossEntropy);
+    const float fill = kMaxFirst ? -INFINITY : 0.0f;
+    const int end = first + slice_len(s, span, cols);  // slice end (exclusive)
+
+    float v[K];
+#pragma unroll
+    for (int c = 0; c < NCHUNK; ++c) {
+        load_window<V, HINT, true>(xr, c * stride + base, cols, &v[c * V], fill);
+        // Columns of the next slice belong to it, not to this one.
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            if (c * stride + base + e >= end) v[c * V + e] = fill;
+    }
+    if constexpr (OP == kResidualLayerNorm) {
+        const T *rr = static_cast<const T *>(a.residual) + off;
+        T *hr = a.h_out ? static_cast<T *>(a.h_out) + off : nullptr;
+#pragma unroll
+        for (int c = 0; c < NCHUNK; ++c) {
+            float r[V];
+            const int i0 = c * stride + base;
+            load_window<V, HINT, true>(rr, i0, cols, r, 0.0f);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float h = is_bf16<T> ? round_to_bf16(v[c * V + e] + r[e]) : v[c * V + e] + r[e];
+                v[c * V + e] = (i0 + e < end) ? h : 0.0f;
+            }
+            if (hr != nullptr) {
+                float o[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) o[e] = v[c * V + e];
+                // Only this slice's columns: the store is guarded by `end`.
+                store_guarded<V, HINT>(hr, i0, end, o);
+            }
+        }
+    }
+
+    Partial2 out = {0.0, 0.0};
+    if constexpr (OP == kRmsNorm) {
+        float t[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) t[k] = v[k] * v[k];
+        out.a = (double)row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds0);
+    } else if constexpr (OP == kSum) {
+        double t[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) t[k] = (double)v[k];
+        out.a = row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, ldsd);
+    } else if constexpr (kMaxFirst) {
+        float t[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) t[k] = v[k];
+        const float m = row_reduce(tree_reduce<K>(t, MaxOp{}), MaxOp{}, rl, lds0);
+#pragma unroll
+        for (int k = 0; k < K; ++k) t[k] = expf(v[k] - m);
+        out.a = (double)m;
+        out.b = (double)row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds1);
+    } else {
+        static_assert(OP == kLayerNorm || OP == kResidualLayerNorm, "unknown operator");
+        const float n = (float)(end - first);
+        float t[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) t[k] = v[k];
+        const float mean = row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds0) / n;
+#pragma unroll
+        for (int c = 0; c < NCHUNK; ++c) {
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float d = v[c * V + e] - mean;
+                t[c * V + e] = (c * stride + base + e < end) ? d * d : 0.0f;
+            }
+        }
+        out.a = (double)mean;
+        out.b = (double)row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds1);
+    }
+    if (threadIdx.x == 0) static_cast<Partial2 *>(a.workspace)[row * gridDim.x + s] = out;
+}
+
+// Merge of the row's `slices` partials, each lane taking every W-th one in
+// slice order, then the fixed-order row reduction.
+template <int OP>
+__device__ __forceinline__ void merge_partials(const Partial2 *p, int slices, int span, int cols,
+                                               const RowLanes<64> &rl, double *ldsd0, double *ldsd1,
+                                               double &stat0, double &stat1) {
+    if constexpr (OP == kRmsNorm || OP == kSum) {
+        double acc = 0.0;
+        for (int j = rl.lane; j < slices; j += rl.W) acc += p[j].a;
+        stat0 = row_reduce(acc, AddOp{}, rl, ldsd0);
+    } else if constexpr (OP == kSoftmax || OP == kCrossEntropy) {
+        double m = -INFINITY;
+        for (int j = rl.lane; j < slices; j += rl.W) m = fmax(m, p[j].a);
+        m = row_reduce(m, MaxOp{}, rl, ldsd0);
+        double z = 0.0;
+        for (int j = rl.lane; j < slices; j += rl.W) z += p[j].b * exp(p[j].a - m);
+        stat0 = m;
+        stat1 = row_reduce(z, AddOp{}, rl, ldsd1);
+    } else {
+        // Chan: mean = sum n_j mean_j / N; M2 = sum (M2_j + n_j (mean_j - mean)^2).
+        double sm = 0.0;
+        for (int j = rl.lane; j < slices; j += rl.W) sm += (double)slice_len(j, span, cols) * p[j].a;
+        const double mean = row_reduce(sm, AddOp{}, rl, ldsd0) / (double)cols;
+        double m2 = 0.0;
+        for (int j = rl.lane; j < slices; j += rl.W) {
+            const double d = p[j].a - mean;
+            m2 += p[j].b + (double)slice_len(j, span, cols) * d * d;
+        }
+        stat0 = mean;
+        stat1 = row_reduce(m2, AddOp{}, rl, ldsd1) / (double)cols;
+    }
+}
+
+template <int OP, int V, int NCHUNK, int HINT, class T>
+__global__ void __launch_bounds__(1024) split_final_kernel(const Args a) {
+    constexpr int K = V * NCHUNK;
+    __shared__ double ldsd0[16];
+    __shared__ double ldsd1[16];
+    const RowLanes<64> rl(a);
+    const int cols = a.cols;
+    const int s = blockIdx.x;
+    const int64_t row = blockIdx.y;
+    const int64_t off = row * (int64_t)cols;
+    const int span = rl.W * K;
+    const int slices = (cols + span - 1) / span;
+    const int first = s * span;
+    const int stride = rl.W * V;
+    const int base = first + rl.lane * V;
+    const int end = first + slice_len(s, span, cols);
+    const Partial2 *p = static_cast<const Partial2 *>(a.workspace) + row * slices;
+    double stat0 = 0.0, stat1 = 0.0;
+    merge_partials<OP>(p, slices, span, cols, rl, ldsd0, ldsd1, stat0, stat1);
+
+    const T *xr = static_cast<const T *>(a.x) + off;
+    if constexpr (OP == kSum) {
+        if (threadIdx.x == 0) a.row_out[row] = (float)stat0;
+        return;
+    } else if constexpr (OP == kCrossEntropy) {
+        if (threadIdx.x == 0) {
+            const int t = a.targets[row];
+            float xt = __builtin_nanf("");
+            if (t >= 0 && t < cols) load_pack<1>(xr + t, &xt);
+            a.row_out[row] = (float)(log(stat1) + stat0 - (double)xt);
+        }
+        return;
+    } else {
+        const T *Wt = static_cast<const T *>(a.w);
+        const T *B = static_cast<const T *>(a.beta);
+        T *Y = static_cast<T *>(a.y) + off;
+        const T *rr = (OP == kResidualLayerNorm) ? static_cast<const T *>(a.residual) + off : nullptr;
+        float scale = 0.0f, shift = 0.0f;
+        if constexpr (OP == kRmsNorm) scale = (float)(1.0 / sqrt(stat0 / (double)cols + (double)a.eps));
+        if constexpr (OP == kSoftmax) {
+            shift = (float)stat0;
+            scale = (float)(1.0 / stat1);
+        }
+        if constexpr (OP == kLayerNorm || OP == kResidualLayerNorm) {
+            shift = (float)stat0;
+            scale = (float)(1.0 / sqrt(stat1 + (double)a.eps));
+        }
+#pragma unroll
+        for (int c = 0; c < NCHUNK; ++c) {
+            const int i0 = c * stride + base;
+            float d[V], w[V], b[V];
+            load_window<V, HINT, true>(xr, i0, cols, d, 0.0f);
+            if constexpr (OP == kResidualLayerNorm) {
+                float r[V];
+                load_window<V, HINT, true>(rr, i0, cols, r, 0.0f);
+#pragma unroll
+                for (int e = 0; e < V; ++e) d[e] = is_bf16<T> ? round_to_bf16(d[e] + r[e]) : d[e] + r[e];
+            }
+            if constexpr (OP == kRmsNorm) {
+                load_window<V>(Wt, i0, cols, w, 0.0f);
+#pragma unroll
+                for (int e = 0; e < V; ++e) d[e] = d[e] * scale * w[e];
+            } else if constexpr (OP == kSoftmax) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) d[e] = expf(d[e] - shift) * scale;
+            } else {
+                load_window<V>(Wt, i0, cols, w, 0.0f);
+                load_window<V>(B, i0, cols, b, 0.0f);
+#pragma unroll
+                for (int e = 0; e < V; ++e) d[e] = (d[e] - shift) * scale * w[e] + b[e];
+            }
+            store_guarded<V, HINT>(Y, i0, end, d);
+        }
+    }
+}
+
 // ---- host-side dispatch over the compiled instances -------------------------------
 
 struct Launch {
@@ -737,6 +963,28 @@ int launch_loop(const Args &a, const Launch &l) {
     return (int)hipGetLastError();
 }
 
+// Split rows: V = 4 (float) or 8 (bfloat16), K = 16 or 32, streaming hints.
+template <int OP, class T>
+int launch_split(const rr_plan &p, const Args &a, const Launch &l) {
+    constexpr int V = is_bf16<T> ? 8 : 4;
+    if (p.v != V || p.cache != 2) return (int)hipErrorInvalidValue;
+    const int span = p.lanes_per_row * p.slots;
+    const unsigned slices = (unsigned)((a.cols + span - 1) / span);
+    const dim3 grid1(slices, (unsigned)a.rows);
+    const dim3 grid2((OP == kSum || OP == kCrossEntropy) ? 1u : slices, (unsigned)a.rows);
+    constexpr int H = hint_of_cache(2);
+    if (p.slots == 16) {
+        hipLaunchKernelGGL((split_partial_kernel<OP, V, 16 / V, H, T>), grid1, l.block, 0, l.stream, a);
+        hipLaunchKernelGGL((split_final_kernel<OP, V, 16 / V, H, T>), grid2, l.block, 0, l.stream, a);
+    } else if (p.slots == 32) {
+        hipLaunchKernelGGL((split_partial_kernel<OP, V, 32 / V, H, T>), grid1, l.block, 0, l.stream, a);
+        hipLaunchKernelGGL((split_final_kernel<OP, V, 32 / V, H, T>), grid2, l.block, 0, l.stream, a);
+    } else {
+        return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
 // Launch `OP` on storage type T with a plan already checked by the planner.
 template <int OP, class T>
 int launch_op(const rr_plan &p, const Args &args, void *stream) {
@@ -751,6 +999,7 @@ int launch_op(const rr_plan &p, const Args &args, void *stream) {
     l.stream = reinterpret_cast<hipStream_t>(stream);
     l.exact = (int64_t)p.lanes_per_row * p.slots == (int64_t)a.cols;
     l.cache = p.cache;
+    if (p.path == RR_PATH_SPLIT) return launch_split<OP, T>(p, a, l);
     if (p.path == RR_PATH_LOOP) {
         switch (p.v) {
             case 1: return launch_loop<OP, 1, T>(a, l);

@@ -19,6 +19,7 @@ struct Args {
     void *y;                 // per-element output, else null
     void *h_out;             // residual LayerNorm h = x + residual, may be null
     float *row_out;          // per-row output (row sum, loss), else null
+    void *workspace;         // split rows: rows x slices partials (16 bytes each), else null
     int64_t rows;
     int32_t cols;
     int32_t lanes_per_row;   // workers per row (power of two)
@@ -43,8 +44,12 @@ int launch_residual_layernorm_bf16(const rr_plan &p, const Args &a, void *stream
 int launch_cross_entropy_bf16(const rr_plan &p, const Args &a, void *stream);
 
 // Planner (plan.cpp; pure host C++).
-// max_v: widest pack the caller's pointer alignment allows (bfloat16 ops).
-int select_plan(int op, int64_t rows, int64_t cols, rr_plan *out, int max_v = 8);
+// max_v: widest pack the caller's pointer alignment allows (bfloat16 ops);
+// workspace_bytes > 0 lets the selector pick a split plan that fits in it.
+int select_plan(int op, int64_t rows, int64_t cols, rr_plan *out, int max_v = 8,
+                int64_t workspace_bytes = 0);
 int check_plan(int op, int64_t rows, int64_t cols, const rr_plan *plan);
+// Workspace a (legal) plan needs: rows x slices x 16 bytes for split plans, else 0.
+int64_t plan_workspace_bytes(int64_t rows, int64_t cols, const rr_plan *plan);
 
 }  // namespace rowred

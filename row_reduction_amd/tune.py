@@ -88,7 +88,7 @@ def host_inputs(op: str, rows: int, cols: int, held_out: bool) -> dict:
 class Case:
     """Device buffers for one (op, shape), replicated into enough sets to run cold."""
 
-    def __init__(self, torch, op, rows, cols, held_out, device, hot=False):
+    def __init__(self, torch, op, rows, cols, held_out, device, hot=False, workspace=False):
         import row_reduction_amd as rr
         self.torch, self.rr, self.op, self.rows, self.cols = torch, rr, op, rows, cols
         h = host_inputs(op, rows, cols, held_out)
@@ -111,6 +111,12 @@ class Case:
             self.nsets = int(min(1024, -(-COLD_BYTES // per_set)))
         self.cold = self.nsets > 1 or per_set >= COLD_BYTES
         self.cold_possible = per_set >= (1 << 20)
+        # Optional split-row workspace (shared by the sets: launches are sequential).
+        self.ws = None
+        if workspace:
+            n = rr.rr_workspace_bytes(op, rows, cols)
+            if n > 0:
+                self.ws = torch.empty(n, dtype=torch.uint8, device=device)
         self.sets = []
         for _ in range(self.nsets):
             s = dict(dev)
@@ -126,19 +132,20 @@ class Case:
     def launch(self, i: int, plan) -> None:
         s, rr = self.sets[i % self.nsets], self.rr
         op, sfx = self.base, ("_bf16" if self.bf16 else "_f32")
+        kw = {"plan": plan, "workspace": self.ws}
         if op == "rmsnorm":
-            getattr(rr, "rmsnorm" + sfx)(s["x"], s["w"], self.eps, y=s["out"], plan=plan)
+            getattr(rr, "rmsnorm" + sfx)(s["x"], s["w"], self.eps, y=s["out"], **kw)
         elif op == "sum":
-            getattr(rr, "row_sum" + sfx)(s["x"], out=s["out"], plan=plan)
+            getattr(rr, "row_sum" + sfx)(s["x"], out=s["out"], **kw)
         elif op == "softmax":
-            getattr(rr, "softmax" + sfx)(s["x"], y=s["out"], plan=plan)
+            getattr(rr, "softmax" + sfx)(s["x"], y=s["out"], **kw)
         elif op == "layernorm":
-            getattr(rr, "layernorm" + sfx)(s["x"], s["w"], s["beta"], self.eps, y=s["out"], plan=plan)
+            getattr(rr, "layernorm" + sfx)(s["x"], s["w"], s["beta"], self.eps, y=s["out"], **kw)
         elif op == "residual_layernorm":
             getattr(rr, "residual_layernorm" + sfx)(s["x"], s["residual"], s["w"], s["beta"], self.eps,
-                                                    y=s["out"], plan=plan)
+                                                    y=s["out"], **kw)
         elif op == "cross_entropy":
-            getattr(rr, "cross_entropy" + sfx)(s["x"], s["targets"], loss=s["out"], plan=plan)
+            getattr(rr, "cross_entropy" + sfx)(s["x"], s["targets"], loss=s["out"], **kw)
 
     def output(self):
         return self.sets[0]["out"]

@@ -9,7 +9,8 @@ import pytest
 import oracle
 from row_reduction_amd import _capi, workloads
 from row_reduction_amd._capi import (RR_ERR_INVALID_ARGUMENT, RR_ERR_UNSUPPORTED, RR_OK,
-                                     RR_PATH_LOOP, RR_PATH_PACKED, RR_PATH_ROW, rr_plan)
+                                     RR_PATH_LOOP, RR_PATH_PACKED, RR_PATH_ROW, RR_PATH_SPLIT,
+                                     rr_plan)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rowred.h")
@@ -29,7 +30,7 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const\s+char\s*\*)\s*(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int64_t|int|const\s+char\s*\*)\s*(\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_documented_entry_points():
@@ -272,3 +273,45 @@ def test_algorithmic_bytes_table():
     assert workloads.algorithmic_bytes("sum", 1024, 4096) == 16781312
     assert workloads.algorithmic_bytes("residual_layernorm", 64, 4096) == 3178496
     assert workloads.algorithmic_bytes("cross_entropy", 17, 257) == 17612
+
+
+# ---------------------------------------------------------------- split rows
+
+def split(lanes, v, slots, cache=2):
+    return rr_plan(RR_PATH_SPLIT, lanes, lanes, 1, v, slots, cache)
+
+
+def test_split_plan_legality(L):
+    rms, rms16 = 0, _capi.OP_IDS["rmsnorm_bf16"]
+    assert L.rr_check_plan(rms, 2, 100003, split(256, 4, 16)) == RR_OK           # 25 slices
+    assert L.rr_check_plan(rms, 2, 4096, split(256, 4, 16)) == RR_ERR_UNSUPPORTED   # one slice
+    assert L.rr_check_plan(rms, 2, 100003, split(256, 2, 16)) == RR_ERR_UNSUPPORTED  # V must be 4
+    assert L.rr_check_plan(rms, 2, 100003, split(256, 4, 8)) == RR_ERR_UNSUPPORTED   # slots 16 or 32
+    assert L.rr_check_plan(rms, 2, 100003, split(256, 4, 16, 0)) == RR_ERR_UNSUPPORTED  # cache 2
+    assert L.rr_check_plan(rms, 2, 100003, split(32, 4, 16)) == RR_ERR_UNSUPPORTED   # >= 64 lanes
+    assert L.rr_check_plan(rms, 2, 64 * 16 * 1025, split(64, 4, 16)) == RR_ERR_UNSUPPORTED  # > 1024 slices
+    assert L.rr_check_plan(rms, 70000, 100003, split(256, 4, 16)) == RR_ERR_UNSUPPORTED  # rows > 65535
+    assert L.rr_check_plan(rms16, 2, 100000, split(256, 8, 16)) == RR_OK
+    assert L.rr_check_plan(rms16, 2, 100003, split(256, 8, 16)) == RR_ERR_UNSUPPORTED  # cols % 8
+
+
+def test_workspace_bytes(L):
+    p = split(256, 4, 16)
+    assert L.rr_workspace_bytes(0, 3, 100003, p) == 3 * 25 * 16
+    assert L.rr_workspace_bytes(0, 3, 4096, plan(RR_PATH_ROW, 256, 256, 4, 16)) == 0
+    assert L.rr_workspace_bytes(0, 3, 4096, p) == -1                  # illegal plan
+    # Selector with unlimited workspace: few long rows split, many rows do not.
+    assert L.rr_workspace_bytes(0, 3, 100003, None) == 3 * 25 * 16
+    assert L.rr_workspace_bytes(0, 4096, 100003, None) == 0
+    assert L.rr_workspace_bytes(0, 3, 4096, None) == 0
+    assert L.rr_workspace_bytes(99, 3, 4096, None) == -1
+
+
+def test_split_needs_workspace_and_alignment(L):
+    p = split(256, 4, 16)
+    assert L.rmsnorm_f32_ex(P, P, P, 3, 100003, 1e-6, p, None) == RR_ERR_UNSUPPORTED
+    assert L.rmsnorm_f32_ws(P, P, P, 3, 100003, 1e-6, p, P, 3 * 25 * 16 - 1, None) == RR_ERR_UNSUPPORTED
+    assert L.rmsnorm_f32_ws(P, P, P, 3, 100003, 1e-6, p, ctypes.c_void_p(0x10008), 4096, None) == \
+        RR_ERR_INVALID_ARGUMENT                                       # workspace not 16-byte aligned
+    assert L.rmsnorm_f32_ws(P, P, P, 3, 100003, 1e-6, None, P, -1, None) == RR_ERR_INVALID_ARGUMENT
+    assert L.cross_entropy_f32_ws(P, P, P, 3, 100003, p, None, 0, None) == RR_ERR_UNSUPPORTED

@@ -1,0 +1,148 @@
+"""GPU parity of the split-row path (several workgroups per row, partials in
+a caller workspace, two launches) against the CPU oracle, for every operator
+in float and bfloat16 storage, with the selector's split plans and explicit
+ones, ragged last slices, determinism, and workspace reuse."""
+import numpy as np
+import pytest
+
+import oracle
+import row_reduction_amd as rr
+from row_reduction_amd import workloads
+from row_reduction_amd._capi import RR_PATH_SPLIT
+
+from parity_util import announce, compare, family_host_inputs, run_oracle
+from test_gpu_bf16 import compare as compare_bf16
+from test_gpu_bf16 import dev_inputs as dev_inputs_bf16
+from test_gpu_bf16 import run_oracle as run_oracle_bf16
+
+pytestmark = pytest.mark.gpu
+
+OPS = list(workloads.OPS)
+SPLIT_SHAPES = [(1, 100003), (3, 40000), (17, 16384), (2, 1 << 20)]
+SPLIT_SHAPES_BF16 = [(1, 100000), (3, 40000), (17, 16384), (2, 1 << 20)]
+
+
+def split_plans(op, rows, cols):
+    """Explicit split plans legal for the shape."""
+    v = 8 if op.endswith("_bf16") else 4
+    out = []
+    for lanes, slots in [(64, 16), (256, 16), (256, 32), (1024, 32)]:
+        p = rr.rr_plan(RR_PATH_SPLIT, lanes, lanes, 1, v, slots, 2)
+        if rr.rr_check_plan(op, rows, cols, p) == 0:
+            out.append(p)
+    return out
+
+
+def run_f32(op, d, plan, ws, gpu_device):
+    import torch
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(gpu_device) if isinstance(v, np.ndarray) else v
+         for k, v in d.items()}
+    if op == "rmsnorm":
+        return {"y": rr.rmsnorm_f32(t["x"], t["w"], t["eps"], plan=plan, workspace=ws)}
+    if op == "sum":
+        return {"out": rr.row_sum_f32(t["x"], plan=plan, workspace=ws)}
+    if op == "softmax":
+        return {"y": rr.softmax_f32(t["x"], plan=plan, workspace=ws)}
+    if op == "layernorm":
+        return {"y": rr.layernorm_f32(t["x"], t["w"], t["beta"], t["eps"], plan=plan, workspace=ws)}
+    if op == "residual_layernorm":
+        h = torch.empty_like(t["x"])
+        y = rr.residual_layernorm_f32(t["x"], t["residual"], t["w"], t["beta"], t["eps"], h_out=h,
+                                      plan=plan, workspace=ws)
+        return {"y": y, "h": h}
+    return {"loss": rr.cross_entropy_f32(t["x"], t["targets"], plan=plan, workspace=ws)}
+
+
+def run_bf16(op, t, plan, ws):
+    import torch
+    eps = workloads.RMSNORM_EPS if op == "rmsnorm" else workloads.LAYERNORM_EPS
+    if op == "rmsnorm":
+        return {"y": rr.rmsnorm_bf16(t["x"], t["gamma"], eps, plan=plan, workspace=ws)}
+    if op == "sum":
+        return {"out": rr.row_sum_bf16(t["x"], plan=plan, workspace=ws)}
+    if op == "softmax":
+        return {"y": rr.softmax_bf16(t["x"], plan=plan, workspace=ws)}
+    if op == "layernorm":
+        return {"y": rr.layernorm_bf16(t["x"], t["gamma"], t["beta"], eps, plan=plan, workspace=ws)}
+    if op == "residual_layernorm":
+        h = torch.empty_like(t["x"])
+        y = rr.residual_layernorm_bf16(t["x"], t["residual"], t["gamma"], t["beta"], eps, h_out=h,
+                                       plan=plan, workspace=ws)
+        return {"y": y, "h": h}
+    return {"loss": rr.cross_entropy_bf16(t["x"], t["targets"], plan=plan, workspace=ws)}
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES)
+@pytest.mark.parametrize("op", OPS)
+def test_split_f32_matches_oracle(gpu_device, op, shape):
+    import torch
+    rows, cols = shape
+    d = family_host_inputs(op, rows, cols, seed=cols % 997)
+    ref = run_oracle(op, d)
+    sel = rr.rr_select_plan(op, rows, cols)
+    nbytes = rr.rr_workspace_bytes(op, rows, cols)
+    assert nbytes > 0, "the selector splits few long rows when given a workspace"
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu_device)
+    announce(f"split {op} {rows}x{cols} auto (workspace {nbytes} B; plain plan {sel.as_dict()})")
+    compare(op, run_f32(op, d, None, ws, gpu_device), ref, f"split {op} {rows}x{cols} auto")
+    for p in split_plans(op, rows, cols):
+        need = rr.rr_workspace_bytes(op, rows, cols, p)
+        wsp = torch.empty(need, dtype=torch.uint8, device=gpu_device)
+        what = f"split {op} {rows}x{cols} w{p.lanes_per_row} k{p.slots}"
+        announce(what)
+        compare(op, run_f32(op, d, p, wsp, gpu_device), ref, what)
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES_BF16)
+@pytest.mark.parametrize("op", OPS)
+def test_split_bf16_matches_oracle(gpu_device, op, shape):
+    import torch
+    rows, cols = shape
+    d = workloads.family_inputs_bf16(rows, cols, seed=cols % 991)
+    eps = workloads.RMSNORM_EPS if op == "rmsnorm" else workloads.LAYERNORM_EPS
+    ref = run_oracle_bf16(op, d, eps)
+    t = dev_inputs_bf16(d, gpu_device)
+    nbytes = rr.rr_workspace_bytes(op + "_bf16", rows, cols)
+    assert nbytes > 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu_device)
+    announce(f"split {op}_bf16 {rows}x{cols} auto")
+    compare_bf16(run_bf16(op, t, None, ws), ref, f"split {op}_bf16 {rows}x{cols} auto")
+    for p in split_plans(op + "_bf16", rows, cols):
+        need = rr.rr_workspace_bytes(op + "_bf16", rows, cols, p)
+        wsp = torch.empty(need, dtype=torch.uint8, device=gpu_device)
+        what = f"split {op}_bf16 {rows}x{cols} w{p.lanes_per_row} k{p.slots}"
+        announce(what)
+        compare_bf16(run_bf16(op, t, p, wsp), ref, what)
+
+
+def test_split_deterministic_and_workspace_reuse(gpu_device):
+    """Fixed merge order: repeated split calls are bit-identical, and one
+    workspace serves calls of different shapes in sequence."""
+    import torch
+    ws = torch.empty(rr.rr_workspace_bytes("softmax", 4, 1 << 20), dtype=torch.uint8, device=gpu_device)
+    for op in OPS:
+        d = family_host_inputs(op, 4, 1 << 20, seed=5)
+        announce(f"split determinism {op}")
+        first = {k: v.clone() for k, v in run_f32(op, d, None, ws, gpu_device).items()}
+        for _ in range(5):
+            again = run_f32(op, d, None, ws, gpu_device)
+            for k in first:
+                assert torch.equal(first[k].view(torch.int32), again[k].view(torch.int32)), op
+    d = family_host_inputs("rmsnorm", 2, 50000, seed=6)
+    compare("rmsnorm", run_f32("rmsnorm", d, None, ws, gpu_device), run_oracle("rmsnorm", d),
+            "split rmsnorm 2x50000 reused workspace")
+
+
+def test_split_in_place_rmsnorm(gpu_device):
+    """y aliasing x is safe for split rows: each slice's final workgroup
+    re-reads only its own columns before storing them."""
+    import torch
+    d = family_host_inputs("rmsnorm", 3, 100003, seed=7)
+    ref = oracle.rmsnorm(d["x"], d["w"], d["eps"])
+    x = torch.from_numpy(d["x"]).to(gpu_device)
+    w = torch.from_numpy(d["w"]).to(gpu_device)
+    ws = torch.empty(rr.rr_workspace_bytes("rmsnorm", 3, 100003), dtype=torch.uint8, device=gpu_device)
+    announce("split rmsnorm in place")
+    rr.rmsnorm_f32(x, w, d["eps"], y=x, workspace=ws)
+    from parity_util import assert_close
+    assert_close(x.cpu().numpy(), ref, "split in place")
