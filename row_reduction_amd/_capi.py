@@ -142,8 +142,8 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
-                f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
-                "or `python row_reduction_amd/build.py` first")
+                f"{LIB_PATH} is not built; run "
+                "`python row_reduction_amd/build.py` first")
         L = ctypes.CDLL(LIB_PATH)
         for name, argtypes in _SIGNATURES.items():
             fn = getattr(L, name)

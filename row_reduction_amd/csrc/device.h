@@ -538,7 +538,12 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
 //
 // One row per workgroup, W = blockDim.x workers, the same ownership map with as
 // many chunks as the row needs. Every pass re-reads the row from memory, one
-// branch-free window load per pack.
+// branch-free window load per pack. Statistics take a single pass: softmax and
+// cross-entropy keep a running (max, sum of exp) per lane, rescaling the sum
+// when the max grows; LayerNorm keeps a running (count, mean, M2) per lane,
+// merging each pack with Chan's formula; lanes then merge in a fixed order.
+// Passes over the row: RMSNorm 2, softmax 2, LayerNorm 2, cross-entropy 1,
+// row sum 1.
 template <int OP, int V, int HINT, class T>
 __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
     const T *Wt = static_cast<const T *>(a.w);
@@ -601,30 +606,30 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
         const double s = row_reduce(acc, AddOp{}, rl, ldsd);
         if (rl.lane == 0) a.row_out[row] = (float)s;
     } else if constexpr (OP == kSoftmax || OP == kCrossEntropy) {
-        float mx = -INFINITY;
+        float m = -INFINITY, z = 0.0f;  // running max and sum of exp(x - m)
         for (int c = 0; c < nchunk; ++c) {
-            float d[V];
-            read(c * stride + base, d, -INFINITY);
-            mx = fmaxf(mx, tree_reduce<V>(d, MaxOp{}));
-        }
-        const float m = row_reduce(mx, MaxOp{}, rl, lds0);
-        float acc = 0.0f;
-        for (int c = 0; c < nchunk; ++c) {
-            float d[V];
+            float d[V], t[V];
             read(c * stride + base, d, -INFINITY);
 #pragma unroll
-            for (int e = 0; e < V; ++e) d[e] = expf(d[e] - m);
-            acc += tree_reduce<V>(d, AddOp{});
+            for (int e = 0; e < V; ++e) t[e] = d[e];
+            const float mn = fmaxf(m, tree_reduce<V>(t, MaxOp{}));
+            if (mn != -INFINITY) {  // missing columns hold -inf: exp gives 0
+#pragma unroll
+                for (int e = 0; e < V; ++e) t[e] = expf(d[e] - mn);
+                z = z * expf(m - mn) + tree_reduce<V>(t, AddOp{});
+                m = mn;
+            }
         }
-        const float z = row_reduce(acc, AddOp{}, rl, lds1);
+        const float mrow = row_reduce(m, MaxOp{}, rl, lds0);
+        const float zrow = row_reduce(m == -INFINITY ? 0.0f : z * expf(m - mrow), AddOp{}, rl, lds1);
         if constexpr (OP == kSoftmax) {
-            const float rz = 1.0f / z;
+            const float rz = 1.0f / zrow;
             for (int c = 0; c < nchunk; ++c) {
                 const int i0 = c * stride + base;
                 float d[V];
                 read(i0, d, -INFINITY);
 #pragma unroll
-                for (int e = 0; e < V; ++e) d[e] = expf(d[e] - m) * rz;
+                for (int e = 0; e < V; ++e) d[e] = expf(d[e] - mrow) * rz;
                 store_guarded<V, HINT>(Y + off, i0, cols, d);
             }
         } else {
@@ -632,31 +637,39 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
                 const int t = a.targets[row];
                 float xt = __builtin_nanf("");
                 if (t >= 0 && t < cols) load_pack<1>(xr + t, &xt);
-                a.row_out[row] = logf(z) + m - xt;
+                a.row_out[row] = logf(zrow) + mrow - xt;
             }
         }
     } else {
         static_assert(OP == kLayerNorm || OP == kResidualLayerNorm, "unknown operator");
-        float acc = 0.0f;
-        for (int c = 0; c < nchunk; ++c) {
-            float d[V];
-            read(c * stride + base, d, 0.0f);
-            acc += tree_reduce<V>(d, AddOp{});
-        }
-        const float mean = row_reduce(acc, AddOp{}, rl, lds0) / (float)cols;
-        float acc2 = 0.0f;
+        float n = 0.0f, mean = 0.0f, m2 = 0.0f;  // running count, mean, sum of squared deviations
         for (int c = 0; c < nchunk; ++c) {
             const int i0 = c * stride + base;
             float d[V];
             read(i0, d, 0.0f);
+            const int left = cols - i0;
+            const float k = (float)(left >= V ? V : (left > 0 ? left : 0));
+            if (k > 0.0f) {
+                float t[V];
 #pragma unroll
-            for (int e = 0; e < V; ++e) {
-                const float dv = d[e] - mean;
-                d[e] = (i0 + e < cols) ? dv * dv : 0.0f;
+                for (int e = 0; e < V; ++e) t[e] = d[e];
+                const float pm = tree_reduce<V>(t, AddOp{}) / k;
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float dv = d[e] - pm;
+                    t[e] = (i0 + e < cols) ? dv * dv : 0.0f;
+                }
+                const float pm2 = tree_reduce<V>(t, AddOp{});
+                const float nn = n + k;
+                const float delta = pm - mean;
+                mean += delta * (k / nn);
+                m2 += pm2 + delta * delta * (n * k / nn);
+                n = nn;
             }
-            acc2 += tree_reduce<V>(d, AddOp{});
         }
-        const float var = row_reduce(acc2, AddOp{}, rl, lds1) / (float)cols;
+        const float rmean = row_reduce(n * mean, AddOp{}, rl, lds0) / (float)cols;
+        const float dev = mean - rmean;
+        const float var = row_reduce(m2 + n * dev * dev, AddOp{}, rl, lds1) / (float)cols;
         const float rstd = rsqrtf(var + a.eps);
         T *hr = (OP == kResidualLayerNorm && a.h_out != nullptr) ? static_cast<T *>(a.h_out) + off : nullptr;
         for (int c = 0; c < nchunk; ++c) {
@@ -667,7 +680,7 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
             load_window<V>(Wt, i0, cols, g, 0.0f);
             load_window<V>(B, i0, cols, b, 0.0f);
 #pragma unroll
-            for (int e = 0; e < V; ++e) d[e] = (d[e] - mean) * rstd * g[e] + b[e];
+            for (int e = 0; e < V; ++e) d[e] = (d[e] - rmean) * rstd * g[e] + b[e];
             store_guarded<V, HINT>(Y + off, i0, cols, d);
         }
     }
