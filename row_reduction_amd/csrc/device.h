@@ -201,43 +201,42 @@ __device__ __forceinline__ void store_one(float *p, float v) { st<HINT>(p, v); }
 template <int HINT>
 __device__ __forceinline__ void store_one(bf16_t *p, float v) { st<HINT>(reinterpret_cast<u16 *>(p), bf16_bits(v)); }
 
-// Pack of V columns starting at i0 of a row with `cols` columns (cols >= V),
-// without branches: the V-wide load always reads the in-bounds window that
-// starts at min(i0, cols - V), and each slot then picks its column out of
-// the window, or `fill` when the column lies past the row end. A complete
-// pack reads exactly its own columns; nothing outside the row is read.
+// Window layout of the pack of V columns that starts at column i0 of a row
+// with `cols` columns (cols >= V), read without branches: the V-wide load
+// always reads the in-bounds window that starts at window_start(i0, cols) =
+// min(i0, cols - V), and slot e holds column window_start + e, which belongs
+// to the pack when it is >= i0. A complete pack's window is the pack itself;
+// the row's last, partial pack reads the row's final V columns and keeps the
+// ones from i0 on; a pack past the row end keeps none. Slots that hold no
+// column of the pack get `fill`. Nothing outside the row is read, and each
+// slot costs one compare and one select.
+template <int V>
+__device__ __forceinline__ int window_start(int i0, int cols) { return i0 < cols - V ? i0 : cols - V; }
+
 template <int V, int HINT = 0, bool STREAM = false, class T>
 __device__ __forceinline__ void load_window(const T *__restrict__ row, int i0, int cols, float *d,
                                             float fill) {
-    if constexpr (V == 1) {
-        float t;
-        load_pack<1, HINT, STREAM>(row + (i0 < cols ? i0 : cols - 1), &t);
-        d[0] = (i0 < cols) ? t : fill;
-    } else {
-        const int start = i0 < cols - V ? i0 : cols - V;
-        const int shift = i0 - start;  // 0 for a complete pack
-        float t[V];
-        load_pack<V, HINT, STREAM>(row + start, t);
+    const int start = window_start<V>(i0, cols);
+    const int lo = i0 - start;  // slots below lo hold columns of earlier packs
+    float t[V];
+    load_pack<V, HINT, STREAM>(row + start, t);
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-            const int p = e + shift;
-            float s = fill;
-#pragma unroll
-            for (int q = V - 1; q >= 0; --q) s = (p == q) ? t[q] : s;
-            d[e] = s;
-        }
-    }
+    for (int e = 0; e < V; ++e) d[e] = (e >= lo) ? t[e] : fill;
 }
 
-// Store of the columns of a pack that lie inside the row.
+// Store of a pack held in the window layout: only the pack's own columns that
+// lie before `end` (the row end, or a slice end on the split path) are written.
 template <int V, int HINT = 0, class T>
-__device__ __forceinline__ void store_guarded(T *__restrict__ row, int i0, int cols, const float *d) {
-    if (i0 + V <= cols) {
-        store_pack<V, HINT>(row + i0, d);
+__device__ __forceinline__ void store_guarded(T *__restrict__ row, int i0, int cols, int end, const float *d) {
+    if (i0 + V <= end) {
+        store_pack<V, HINT>(row + i0, d);  // complete pack: the window starts at i0
     } else {
+        const int start = window_start<V>(i0, cols);
 #pragma unroll
-        for (int e = 0; e < V; ++e)
-            if (i0 + e < cols) store_one<HINT>(row + i0 + e, d[e]);
+        for (int e = 0; e < V; ++e) {
+            const int j = start + e;
+            if (j >= i0 && j < end) store_one<HINT>(row + j, d[e]);
+        }
     }
 }
 
@@ -253,7 +252,7 @@ __device__ __forceinline__ void load_slots(const T *__restrict__ row, int i0, in
 template <int V, bool EXACT, int HINT = 0, class T>
 __device__ __forceinline__ void store_slots(T *__restrict__ row, int i0, int cols, const float *d) {
     if constexpr (EXACT) store_pack<V, HINT>(row + i0, d);
-    else store_guarded<V, HINT>(row, i0, cols, d);
+    else store_guarded<V, HINT>(row, i0, cols, cols, d);
 }
 
 // ---- combine operations ------------------------------------------------------
@@ -514,7 +513,8 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const float d = v[c * V + e] - mean;
-                v[c * V + e] = (EXACT || c * stride + base + e < cols) ? d : 0.0f;
+                const int i0 = c * stride + base;
+                v[c * V + e] = (EXACT || window_start<V>(i0, cols) + e >= i0) ? d : 0.0f;
             }
         }
 #pragma unroll
@@ -597,7 +597,7 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
             load_window<V>(Wt, i0, cols, wv, 0.0f);
 #pragma unroll
             for (int e = 0; e < V; ++e) d[e] = d[e] * inv * wv[e];
-            store_guarded<V, HINT>(Y + off, i0, cols, d);
+            store_guarded<V, HINT>(Y + off, i0, cols, cols, d);
         }
     } else if constexpr (OP == kSum) {
         double acc = 0.0;
@@ -636,7 +636,7 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
                 read(i0, d, -INFINITY);
 #pragma unroll
                 for (int e = 0; e < V; ++e) d[e] = exp_nonpos(d[e] - mrow) * rz;
-                store_guarded<V, HINT>(Y + off, i0, cols, d);
+                store_guarded<V, HINT>(Y + off, i0, cols, cols, d);
             }
         } else {
             if (rl.lane == 0) {
@@ -663,7 +663,7 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
                     const float dv = d[e] - pm;
-                    t[e] = (i0 + e < cols) ? dv * dv : 0.0f;
+                    t[e] = (window_start<V>(i0, cols) + e >= i0) ? dv * dv : 0.0f;
                 }
                 const float pm2 = tree_reduce<V>(t, AddOp{});
                 const float nn = n + k;
@@ -682,12 +682,12 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
             const int i0 = c * stride + base;
             float d[V], g[V], b[V];
             read(i0, d, 0.0f);
-            if (hr != nullptr) store_guarded<V, HINT>(hr, i0, cols, d);
+            if (hr != nullptr) store_guarded<V, HINT>(hr, i0, cols, cols, d);
             load_window<V>(Wt, i0, cols, g, 0.0f);
             load_window<V>(B, i0, cols, b, 0.0f);
 #pragma unroll
             for (int e = 0; e < V; ++e) d[e] = (d[e] - rmean) * rstd * g[e] + b[e];
-            store_guarded<V, HINT>(Y + off, i0, cols, d);
+            store_guarded<V, HINT>(Y + off, i0, cols, cols, d);
         }
     }
 }
@@ -738,11 +738,13 @@ __global__ void __launch_bounds__(1024) split_partial_kernel(const Args a) {
     float v[K];
 #pragma unroll
     for (int c = 0; c < NCHUNK; ++c) {
-        load_window<V, HINT, true>(xr, c * stride + base, cols, &v[c * V], fill);
+        const int i0 = c * stride + base;
+        load_window<V, HINT, true>(xr, i0, cols, &v[c * V], fill);
         // Columns of the next slice belong to it, not to this one.
+        const int start = window_start<V>(i0, cols);
 #pragma unroll
         for (int e = 0; e < V; ++e)
-            if (c * stride + base + e >= end) v[c * V + e] = fill;
+            if (start + e >= end) v[c * V + e] = fill;
     }
     if constexpr (OP == kResidualLayerNorm) {
         const T *rr = static_cast<const T *>(a.residual) + off;
@@ -755,14 +757,15 @@ __global__ void __launch_bounds__(1024) split_partial_kernel(const Args a) {
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const float h = is_bf16<T> ? round_to_bf16(v[c * V + e] + r[e]) : v[c * V + e] + r[e];
-                v[c * V + e] = (i0 + e < end) ? h : 0.0f;
+                const int j = window_start<V>(i0, cols) + e;
+                v[c * V + e] = (j >= i0 && j < end) ? h : 0.0f;
             }
             if (hr != nullptr) {
                 float o[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e) o[e] = v[c * V + e];
                 // Only this slice's columns: the store is guarded by `end`.
-                store_guarded<V, HINT>(hr, i0, end, o);
+                store_guarded<V, HINT>(hr, i0, cols, end, o);
             }
         }
     }
@@ -799,7 +802,8 @@ __global__ void __launch_bounds__(1024) split_partial_kernel(const Args a) {
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const float d = v[c * V + e] - mean;
-                t[c * V + e] = (c * stride + base + e < end) ? d * d : 0.0f;
+                const int i0 = c * stride + base, j = window_start<V>(i0, cols) + e;
+                t[c * V + e] = (j >= i0 && j < end) ? d * d : 0.0f;
             }
         }
         out.a = (double)mean;
@@ -912,7 +916,7 @@ __global__ void __launch_bounds__(1024) split_final_kernel(const Args a) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) d[e] = (d[e] - shift) * scale * w[e] + b[e];
             }
-            store_guarded<V, HINT>(Y, i0, end, d);
+            store_guarded<V, HINT>(Y, i0, cols, end, d);
         }
     }
 }

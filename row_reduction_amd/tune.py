@@ -23,6 +23,7 @@ that no launch finds its data cached.
 
 Usage:
   python -m row_reduction_amd.tune --out search.json [--ops rmsnorm,...] [--shapes 1x127,...]
+                                   [--caches all|by-footprint|0,2]
   python -m row_reduction_amd.tune --replay search.json --out replay.json
   python -m row_reduction_amd.tune --emit-table replay.json   # writes csrc/plan_table.inc
   python -m row_reduction_amd.tune --summarize search.json replay.json
@@ -198,9 +199,9 @@ def close(a, b) -> bool:
     """Outputs of two plans agree: float within 2e-5 relative, bfloat16 within
     one unit in the last place (2^-7 relative)."""
     rel = 2.0 ** -7 if a.dtype != b.dtype or str(a.dtype) == "torch.bfloat16" else 2e-5
-    a = a.double().cpu().numpy()
-    b = b.double().cpu().numpy()
-    return bool(np.all(np.abs(a - b) <= 2e-5 + rel * np.abs(b)))
+    a = a.double()
+    b = b.double()
+    return bool(((a - b).abs() <= 2e-5 + rel * b.abs()).all().item())
 
 
 def measure(torch, case: Case, candidates: dict, rounds: int, samples: int) -> dict:
@@ -253,8 +254,14 @@ def run_search(args) -> dict:
             rows, cols = map(int, shape.split("x"))
             log(f"search {op} {shape}")
             case = Case(torch, op, rows, cols, False, device)
-            cands = {plans.plan_key(p): p for p in plans.candidate_plans(op, rows, cols,
-                                                                           caches=plans.CACHES)}
+            caches = plans.CACHES
+            if args.caches == "by-footprint":
+                # One policy per case: non-temporal row data when the working
+                # set is timed cold, default caching when it stays resident.
+                caches = (2,) if case.cold else (0,)
+            elif args.caches != "all":
+                caches = tuple(int(c) for c in args.caches.split(","))
+            cands = {plans.plan_key(p): p for p in plans.candidate_plans(op, rows, cols, caches=caches)}
             res = measure(torch, case, cands, args.rounds, args.samples)
             timed = {k: v for k, v in res.items() if "us" in v}
             best = min(timed, key=lambda k: timed[k]["us"])
@@ -381,6 +388,8 @@ def main() -> int:
     ap.add_argument("--shapes", default=",".join(DEFAULT_SHAPES))
     ap.add_argument("--rounds", type=int, default=2)
     ap.add_argument("--samples", type=int, default=5)
+    ap.add_argument("--caches", default="all",
+                    help="cache policies searched: all, by-footprint (2 when timed cold, else 0), or a list")
     ap.add_argument("--replay", help="search result to re-measure on held-out inputs")
     ap.add_argument("--emit-table", help="replay result to freeze into plan_table.inc")
     ap.add_argument("--summarize", nargs=2, metavar=("SEARCH", "REPLAY"),
