@@ -81,8 +81,10 @@ typedef enum rr_op {
  *   RR_PATH_ROW:    lanes_per_row >= 64 — one row spans lanes_per_row/64 whole
  *                   wavefronts (combined through LDS with one barrier per
  *                   reduction); a workgroup may hold several rows.
- *   RR_PATH_LOOP:   one row per workgroup, values are re-read from memory
- *                   instead of kept in registers; any cols.
+ *   RR_PATH_LOOP:   one row per workgroup, any cols: statistics in one pass
+ *                   over the row, then (RMSNorm, softmax, LayerNorm,
+ *                   residual LayerNorm) a second pass that re-reads the
+ *                   values not kept in registers.
  *   RR_PATH_SPLIT:  a row is cut into S = ceil(cols / (lanes_per_row * slots))
  *                   slices, one workgroup each (2 <= S <= 1024, rows <= 65535):
  *                   a first launch keeps each slice in registers and writes
@@ -115,10 +117,13 @@ typedef enum rr_path {
  *                   pack, at most 16 bytes)
  *   slots           values each worker keeps in registers: chunks * v with
  *                   chunks in {1, 2, 4, 8} and slots <= 32;
- *                   cols <= lanes_per_row * slots. 0 on the LOOP path.
+ *                   cols <= lanes_per_row * slots. On the LOOP path the
+ *                   values kept between the two passes: 0, or 32 for the
+ *                   two-pass operators with v >= 4.
  *   cache           cache policy for the row data: 0 = default; 1 = output
  *                   stores non-temporal; 2 = row loads (x, residual) and
- *                   output stores non-temporal. Weights (w, gamma, beta) are
+ *                   output stores non-temporal (on the LOOP path only the
+ *                   last pass's loads). Weights (w, gamma, beta) are
  *                   always loaded with the default policy. Results do not
  *                   depend on it. */
 typedef struct rr_plan {

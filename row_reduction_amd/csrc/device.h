@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -543,14 +544,17 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
 // ---- streaming kernel for rows beyond the register budget ------------------------
 //
 // One row per workgroup, W = blockDim.x workers, the same ownership map with as
-// many chunks as the row needs. Every pass re-reads the row from memory, one
-// branch-free window load per pack. Statistics take a single pass: softmax and
+// many chunks as the row needs. Statistics take a single pass: softmax and
 // cross-entropy keep a running (max, sum of exp) per lane, rescaling the sum
 // when the max grows; LayerNorm keeps a running (count, mean, M2) per lane,
 // merging each pack with Chan's formula; lanes then merge in a fixed order.
 // Passes over the row: RMSNorm 2, softmax 2, LayerNorm 2, cross-entropy 1,
-// row sum 1.
-template <int OP, int V, int HINT, class T>
+// row sum 1. The first KEEP chunks of a lane (KEEP * V register slots) stay
+// in registers between the two passes, so the second pass re-reads only the
+// rest of the row; the chunks are loaded one after another, every pack in
+// bounds (a pack past the row end reads the row's last window and keeps none
+// of it).
+template <int OP, int V, int KEEP, int HINT, class T>
 __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
     const T *Wt = static_cast<const T *>(a.w);
     const T *B = static_cast<const T *>(a.beta);
@@ -567,39 +571,75 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
     const int nchunk = (cols + stride - 1) / stride;
     const T *xr = static_cast<const T *>(a.x) + off;
     const T *rr = (OP == kResidualLayerNorm) ? static_cast<const T *>(a.residual) + off : nullptr;
+    constexpr int kKeep = KEEP > 0 ? KEEP * V : 1;
+    float keep[kKeep];  // chunks 0 .. KEEP-1 of this lane
 
     // Pack of the row's values (x, or x + residual for residual LayerNorm).
-    auto read = [&](int i0, float *d, float fill) {
-        load_window<V, HINT, true>(xr, i0, cols, d, fill);
+    // The last pass over the row may stream it past the caches (cache policy
+    // 2); an earlier pass loads it normally so that the re-read can still
+    // find it in the last-level cache.
+    auto read_pass = [&](auto last, int i0, float *d, float fill) {
+        constexpr bool kLast = decltype(last)::value;
+        load_window<V, HINT, kLast>(xr, i0, cols, d, fill);
         if constexpr (OP == kResidualLayerNorm) {
             float r[V];
-            load_window<V, HINT, true>(rr, i0, cols, r, 0.0f);
+            load_window<V, HINT, kLast>(rr, i0, cols, r, 0.0f);
 #pragma unroll
             for (int e = 0; e < V; ++e) d[e] = is_bf16<T> ? round_to_bf16(d[e] + r[e]) : d[e] + r[e];
+        }
+    };
+    auto read_first = [&](int i0, float *d, float fill) { read_pass(std::false_type{}, i0, d, fill); };
+    auto read = [&](int i0, float *d, float fill) { read_pass(std::true_type{}, i0, d, fill); };
+    // First pass, chunk c: kept chunks are loaded into `keep` (all of them
+    // issued before any is used), the others into `d`.
+    auto first_pass = [&](auto visit, float fill) {
+#pragma unroll
+        for (int c = 0; c < KEEP; ++c) read_first(c * stride + base, &keep[c * V], fill);
+#pragma unroll
+        for (int c = 0; c < KEEP; ++c) visit(c * stride + base, &keep[c * V]);
+        for (int c = KEEP; c < nchunk; ++c) {
+            float d[V];
+            read_first(c * stride + base, d, fill);
+            visit(c * stride + base, d);
+        }
+    };
+    // Second pass: kept chunks come from registers, the others are re-read.
+    auto second_pass = [&](auto emit, float fill) {
+#pragma unroll
+        for (int c = 0; c < KEEP; ++c) {
+            if (c < nchunk) {
+                float d[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) d[e] = keep[c * V + e];
+                emit(c * stride + base, d);
+            }
+        }
+        for (int c = KEEP; c < nchunk; ++c) {
+            float d[V];
+            read(c * stride + base, d, fill);
+            emit(c * stride + base, d);
         }
     };
 
     if constexpr (OP == kRmsNorm) {
         float acc = 0.0f;
-        for (int c = 0; c < nchunk; ++c) {
-            float d[V];
-            read(c * stride + base, d, 0.0f);
+        first_pass([&](int, const float *d) {
+            float t[V];
 #pragma unroll
-            for (int e = 0; e < V; ++e) d[e] = d[e] * d[e];
-            acc += tree_reduce<V>(d, AddOp{});
-        }
+            for (int e = 0; e < V; ++e) t[e] = d[e] * d[e];
+            acc += tree_reduce<V>(t, AddOp{});
+        }, 0.0f);
         const float ss = row_reduce(acc, AddOp{}, rl, lds0);
         const float inv = rsqrtf(ss / (float)cols + a.eps);
-        for (int c = 0; c < nchunk; ++c) {
-            const int i0 = c * stride + base;
-            float d[V], wv[V];
-            read(i0, d, 0.0f);
+        second_pass([&](int i0, float *d) {
+            float wv[V];
             load_window<V>(Wt, i0, cols, wv, 0.0f);
 #pragma unroll
             for (int e = 0; e < V; ++e) d[e] = d[e] * inv * wv[e];
             store_guarded<V, HINT>(Y + off, i0, cols, cols, d);
-        }
+        }, 0.0f);
     } else if constexpr (OP == kSum) {
+        static_assert(KEEP == 0, "one pass: nothing to keep");
         double acc = 0.0;
         for (int c = 0; c < nchunk; ++c) {
             float d[V];
@@ -612,10 +652,10 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
         const double s = row_reduce(acc, AddOp{}, rl, ldsd);
         if (rl.lane == 0) a.row_out[row] = (float)s;
     } else if constexpr (OP == kSoftmax || OP == kCrossEntropy) {
+        static_assert(OP == kSoftmax || KEEP == 0, "one pass: nothing to keep");
         float m = -INFINITY, z = 0.0f;  // running max and sum of exp(x - m)
-        for (int c = 0; c < nchunk; ++c) {
-            float d[V], t[V];
-            read(c * stride + base, d, -INFINITY);
+        auto visit = [&](int, const float *d) {
+            float t[V];
 #pragma unroll
             for (int e = 0; e < V; ++e) t[e] = d[e];
             const float mn = fmaxf(m, tree_reduce<V>(t, MaxOp{}));
@@ -625,19 +665,25 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
                 z = z * exp_nonpos(m - mn) + tree_reduce<V>(t, AddOp{});
                 m = mn;
             }
+        };
+        if constexpr (OP == kSoftmax) {
+            first_pass(visit, -INFINITY);
+        } else {
+            for (int c = 0; c < nchunk; ++c) {
+                float d[V];
+                read(c * stride + base, d, -INFINITY);
+                visit(0, d);
+            }
         }
         const float mrow = row_reduce(m, MaxOp{}, rl, lds0);
         const float zrow = row_reduce(m == -INFINITY ? 0.0f : z * exp_nonpos(m - mrow), AddOp{}, rl, lds1);
         if constexpr (OP == kSoftmax) {
             const float rz = 1.0f / zrow;
-            for (int c = 0; c < nchunk; ++c) {
-                const int i0 = c * stride + base;
-                float d[V];
-                read(i0, d, -INFINITY);
+            second_pass([&](int i0, float *d) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) d[e] = exp_nonpos(d[e] - mrow) * rz;
                 store_guarded<V, HINT>(Y + off, i0, cols, cols, d);
-            }
+            }, -INFINITY);
         } else {
             if (rl.lane == 0) {
                 const int t = a.targets[row];
@@ -649,10 +695,7 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
     } else {
         static_assert(OP == kLayerNorm || OP == kResidualLayerNorm, "unknown operator");
         float n = 0.0f, mean = 0.0f, m2 = 0.0f;  // running count, mean, sum of squared deviations
-        for (int c = 0; c < nchunk; ++c) {
-            const int i0 = c * stride + base;
-            float d[V];
-            read(i0, d, 0.0f);
+        first_pass([&](int i0, const float *d) {
             const int left = cols - i0;
             const float k = (float)(left >= V ? V : (left > 0 ? left : 0));
             if (k > 0.0f) {
@@ -672,23 +715,21 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
                 m2 += pm2 + delta * delta * (n * k / nn);
                 n = nn;
             }
-        }
+        }, 0.0f);
         const float rmean = row_reduce(n * mean, AddOp{}, rl, lds0) / (float)cols;
         const float dev = mean - rmean;
         const float var = row_reduce(m2 + n * dev * dev, AddOp{}, rl, lds1) / (float)cols;
         const float rstd = rsqrtf(var + a.eps);
         T *hr = (OP == kResidualLayerNorm && a.h_out != nullptr) ? static_cast<T *>(a.h_out) + off : nullptr;
-        for (int c = 0; c < nchunk; ++c) {
-            const int i0 = c * stride + base;
-            float d[V], g[V], b[V];
-            read(i0, d, 0.0f);
+        second_pass([&](int i0, float *d) {
+            float g[V], b[V];
             if (hr != nullptr) store_guarded<V, HINT>(hr, i0, cols, cols, d);
             load_window<V>(Wt, i0, cols, g, 0.0f);
             load_window<V>(B, i0, cols, b, 0.0f);
 #pragma unroll
             for (int e = 0; e < V; ++e) d[e] = (d[e] - rmean) * rstd * g[e] + b[e];
             store_guarded<V, HINT>(Y + off, i0, cols, cols, d);
-        }
+        }, 0.0f);
     }
 }
 
@@ -975,15 +1016,26 @@ int launch_by_v(int v, int chunks, const Args &a, const Launch &l) {
     }
 }
 
-template <int OP, int V, class T>
-int launch_loop(const Args &a, const Launch &l) {
+template <int OP, int V, int KEEP, class T>
+int launch_loop_keep(const Args &a, const Launch &l) {
     switch (l.cache) {
-        case 0: hipLaunchKernelGGL((loop_kernel<OP, V, hint_of_cache(0), T>), l.grid, l.block, 0, l.stream, a); break;
-        case 1: hipLaunchKernelGGL((loop_kernel<OP, V, hint_of_cache(1), T>), l.grid, l.block, 0, l.stream, a); break;
-        case 2: hipLaunchKernelGGL((loop_kernel<OP, V, hint_of_cache(2), T>), l.grid, l.block, 0, l.stream, a); break;
+        case 0: hipLaunchKernelGGL((loop_kernel<OP, V, KEEP, hint_of_cache(0), T>), l.grid, l.block, 0, l.stream, a); break;
+        case 1: hipLaunchKernelGGL((loop_kernel<OP, V, KEEP, hint_of_cache(1), T>), l.grid, l.block, 0, l.stream, a); break;
+        case 2: hipLaunchKernelGGL((loop_kernel<OP, V, KEEP, hint_of_cache(2), T>), l.grid, l.block, 0, l.stream, a); break;
         default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();
+}
+
+// Streaming plans keep 0 or 32 register slots per lane (the latter for the
+// two-pass operators at V >= 4: 32 / V chunks).
+template <int OP, int V, class T>
+int launch_loop(int slots, const Args &a, const Launch &l) {
+    if (slots == 0) return launch_loop_keep<OP, V, 0, T>(a, l);
+    if constexpr (V >= 4 && OP != kSum && OP != kCrossEntropy) {
+        if (slots == 32) return launch_loop_keep<OP, V, 32 / V, T>(a, l);
+    }
+    return (int)hipErrorInvalidValue;
 }
 
 // Split rows: V = 4 (float) or 8 (bfloat16), K = 16 or 32, streaming hints.
@@ -1025,11 +1077,11 @@ int launch_op(const rr_plan &p, const Args &args, void *stream) {
     if (p.path == RR_PATH_SPLIT) return launch_split<OP, T>(p, a, l);
     if (p.path == RR_PATH_LOOP) {
         switch (p.v) {
-            case 1: return launch_loop<OP, 1, T>(a, l);
-            case 2: return launch_loop<OP, 2, T>(a, l);
-            case 4: return launch_loop<OP, 4, T>(a, l);
+            case 1: return launch_loop<OP, 1, T>(p.slots, a, l);
+            case 2: return launch_loop<OP, 2, T>(p.slots, a, l);
+            case 4: return launch_loop<OP, 4, T>(p.slots, a, l);
             case 8:
-                if constexpr (is_bf16<T>) return launch_loop<OP, 8, T>(a, l);
+                if constexpr (is_bf16<T>) return launch_loop<OP, 8, T>(p.slots, a, l);
                 else return (int)hipErrorInvalidValue;
             default: return (int)hipErrorInvalidValue;
         }

@@ -21,6 +21,7 @@ VS = (1, 2, 4)
 VS_BF16 = (1, 2, 4, 8)
 CHUNKS = (1, 2, 4, 8)
 LOOP_BLOCKS = (256, 1024)
+LOOP_KEPT_SLOTS = (0, 32)   # streaming: register slots kept between the two passes
 CACHES = (0, 1, 2)
 
 
@@ -62,7 +63,8 @@ def candidate_plans(op: str, rows: int, cols: int, include_loop: bool = True,
     if include_loop:
         for block in LOOP_BLOCKS:
             for v in vs:
-                add(rr_plan(RR_PATH_LOOP, block, block, 1, v, 0))
+                for kept in LOOP_KEPT_SLOTS:
+                    add(rr_plan(RR_PATH_LOOP, block, block, 1, v, kept))
     return out
 
 

@@ -164,7 +164,8 @@ ILLEGAL = [
     plan(RR_PATH_ROW, 256, 32, 4, 32),         # ROW needs >= 64 lanes
     plan(RR_PATH_PACKED, 256, 64, 4, 16),      # PACKED needs < 64 lanes
     plan(RR_PATH_LOOP, 256, 128, 4, 0),        # LOOP: one row per group
-    plan(RR_PATH_LOOP, 256, 256, 4, 16),       # LOOP keeps no slots
+    plan(RR_PATH_LOOP, 256, 256, 4, 16),       # LOOP keeps 0 or 32 slots
+    plan(RR_PATH_LOOP, 256, 256, 2, 32),       # LOOP keeps slots only at V >= 4
     rr_plan(RR_PATH_ROW, 256, 128, 1, 4, 16),  # rows_per_group inconsistent
     rr_plan(7, 256, 256, 1, 4, 16),            # unknown path
     rr_plan(RR_PATH_ROW, 256, 256, 1, 4, 16, 3),   # unknown cache policy
@@ -204,6 +205,17 @@ def test_bf16_explicit_plan_needs_pointer_alignment(L):
     assert L.softmax_bf16_ex(P, p2, 4, 128, wide, None) == RR_ERR_UNSUPPORTED
 
 
+def test_streaming_kept_slots_only_for_two_pass_operators(L):
+    kept = plan(RR_PATH_LOOP, 1024, 1024, 4, 32)
+    for op in ("rmsnorm", "softmax", "layernorm", "residual_layernorm"):
+        assert L.rr_check_plan(_capi.OP_IDS[op], 3, 100000, kept) == RR_OK
+    for op in ("sum", "cross_entropy"):
+        assert L.rr_check_plan(_capi.OP_IDS[op], 3, 100000, kept) == RR_ERR_UNSUPPORTED
+    kept8 = plan(RR_PATH_LOOP, 1024, 1024, 8, 32)
+    assert L.rr_check_plan(_capi.OP_IDS["softmax_bf16"], 3, 100000, kept8) == RR_OK
+    assert L.rr_check_plan(_capi.OP_IDS["cross_entropy_bf16"], 3, 100000, kept8) == RR_ERR_UNSUPPORTED
+
+
 def test_v_wider_than_row_is_rejected(L):
     assert L.rr_check_plan(0, 1, 3, plan(RR_PATH_PACKED, 64, 8, 4, 4)) == RR_ERR_UNSUPPORTED
     assert L.rr_check_plan(0, 1, 3, plan(RR_PATH_PACKED, 64, 8, 2, 2)) == RR_OK
@@ -239,7 +251,8 @@ def test_selected_plans_are_legal_and_cover_the_row(L, op, rows, cols):
         assert oracle.slot_bound(cols, p.lanes_per_row, p.v) <= p.slots
         assert p.lanes_per_row * p.slots >= cols
     else:
-        assert cols > 1024 * 32 or p.slots == 0
+        assert cols > 1024 * 32
+        assert p.slots in (0, 32)
 
 
 def test_page_packing_arithmetic(L):

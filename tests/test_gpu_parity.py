@@ -111,10 +111,29 @@ def test_streaming_path_beyond_register_budget(gpu_device, op, cols):
     compare(op, run_gpu(op, d, with_h=True), ref, f"{op} {rows}x{cols} selected")
     for v in (1, 2, 4):
         for block in (256, 1024):
-            lp = rr.rr_plan(2, block, block, 1, v, 0)
-            what = f"{op} {rows}x{cols} {plans.plan_key(lp)}"
-            announce(what)
-            compare(op, run_gpu(op, d, plan=lp, with_h=True), ref, what)
+            for kept in (0, 32):
+                lp = rr.rr_plan(2, block, block, 1, v, kept)
+                if rr.rr_check_plan(op, rows, cols, lp) != 0:
+                    continue
+                what = f"{op} {rows}x{cols} {plans.plan_key(lp)}"
+                announce(what)
+                compare(op, run_gpu(op, d, plan=lp, with_h=True), ref, what)
+
+
+@pytest.mark.parametrize("op", ["rmsnorm", "softmax", "layernorm", "residual_layernorm"])
+@pytest.mark.parametrize("cols", [4, 129, 1000, 4096, 5000, 8191])
+def test_streaming_kept_slots_on_short_rows(gpu_device, op, cols):
+    """Kept register chunks beyond the row's last chunk (fewer chunks than the
+    plan keeps) read in bounds, count nothing and store nothing."""
+    rows = 5
+    a = family_host_inputs(op, rows, cols, seed=19)
+    ref = run_oracle(op, a)
+    d = to_dev(a, gpu_device)
+    for block in (256, 1024):
+        lp = rr.rr_plan(2, block, block, 1, 4, 32)
+        what = f"{op} {rows}x{cols} {plans.plan_key(lp)}"
+        announce(what)
+        compare(op, run_gpu(op, d, plan=lp, with_h=True), ref, what)
 
 
 # ---------------------------------------------------------------- semantics and special cases
