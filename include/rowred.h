@@ -280,10 +280,45 @@ int cross_entropy_bf16_ws(const uint16_t *logits, const int32_t *targets, float 
                           const rr_plan *plan, void *workspace, int64_t workspace_bytes, void *stream);
 
 /* Plan the library would use for (op, rows, cols): the measured per-shape
- * table entry when one exists, else the built-in rule. Pure host function;
- * no GPU needed. Returns RR_ERR_INVALID_ARGUMENT for an unknown op, rows < 0,
- * cols <= 0 or out == NULL, RR_ERR_UNSUPPORTED for cols > 2^31-1. */
+ * table entry when one exists, else the analytic model's cheapest legal
+ * candidate (see rr_model_time_us). Pure host function; no GPU needed.
+ * Returns RR_ERR_INVALID_ARGUMENT for an unknown op, rows < 0, cols <= 0 or
+ * out == NULL, RR_ERR_UNSUPPORTED for cols > 2^31-1. The selected plan is
+ * the one the plain entry points launch for suitably aligned pointers (the
+ * *_ws forms with a large enough workspace may split few long rows instead). */
 int rr_select_plan(int op, int64_t rows, int64_t cols, rr_plan *out);
+
+/* Where a plan comes from (rr_select_plan_from).
+ *   RR_PLAN_AUTO   what rr_select_plan returns
+ *   RR_PLAN_TABLE  the frozen table of measured winners (RR_ERR_UNSUPPORTED
+ *                  when the shape is not listed)
+ *   RR_PLAN_MODEL  the analytic model's cheapest legal candidate
+ *   RR_PLAN_RULE   the built-in rule the model replaced (kept for comparison) */
+typedef enum rr_plan_source {
+    RR_PLAN_AUTO = 0,
+    RR_PLAN_TABLE = 1,
+    RR_PLAN_MODEL = 2,
+    RR_PLAN_RULE = 3
+} rr_plan_source;
+
+/* The plan of one source for (op, rows, cols), for full-alignment pointers.
+ * Errors as rr_select_plan, plus RR_ERR_INVALID_ARGUMENT for an unknown
+ * source. Pure host. */
+int rr_select_plan_from(int op, int64_t rows, int64_t cols, int source, rr_plan *out);
+
+/* Analytic cost model: predicted microseconds per launch of a legal
+ * single-launch plan (PACKED, ROW or LOOP) on an MI355X (gfx950, 256 CUs),
+ * launch floor included; -1.0 for an illegal plan, a split plan, or bad
+ * arguments. Terms (after the LuisaCompute notes, "Consecutive-worker
+ * reduction layout checkpoint", section "Evidence and what remains", which
+ * ask for active groups and pack-width behaviour to be priced, and the MPP
+ * memory notes' occupancy term): algorithmic bytes over a rate bounded by
+ * HBM and by the bytes resident lanes keep in flight; rounds of resident
+ * workgroups times a per-group latency chain; total lane-instructions; wave
+ * and workgroup dispatch. Constants are fitted to the plan search's timings
+ * (row_reduction_amd/data/plan_timings.csv). Meant for ranking plans of one
+ * shape; absolute values are approximate. Pure host. */
+double rr_model_time_us(int op, int64_t rows, int64_t cols, const rr_plan *plan);
 
 /* RR_OK if `plan` is legal for (op, rows, cols), else RR_ERR_UNSUPPORTED
  * (RR_ERR_INVALID_ARGUMENT for bad op / shape / NULL plan). Pure host. */

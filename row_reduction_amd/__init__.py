@@ -20,7 +20,8 @@ __all__ = [
     "residual_layernorm_f32", "cross_entropy_f32",
     "rmsnorm_bf16", "row_sum_bf16", "softmax_bf16", "layernorm_bf16",
     "residual_layernorm_bf16", "cross_entropy_bf16",
-    "rr_select_plan", "rr_check_plan", "rr_status_string", "rr_copy_f32", "rr_empty_kernel",
+    "rr_select_plan", "rr_select_plan_from", "rr_model_time_us", "rr_check_plan", "rr_status_string",
+    "rr_copy_f32", "rr_empty_kernel",
     "rr_workspace_bytes", "workspace_for",
     "rr_plan", "RowRedError", "OP_IDS",
 ]
@@ -287,6 +288,23 @@ def rr_select_plan(op, rows, cols) -> rr_plan:
     p = rr_plan()
     _capi.check("rr_select_plan", _capi.lib().rr_select_plan(op_id, rows, cols, p))
     return p
+
+
+def rr_select_plan_from(op, rows, cols, source) -> rr_plan:
+    """Plan of one source for (op, rows, cols): "auto", "table", "model" or
+    "rule" (or an rr_plan_source value)."""
+    src = {"auto": 0, "table": 1, "model": 2, "rule": 3}.get(source, source)
+    op_id = OP_IDS[op] if isinstance(op, str) else int(op)
+    p = rr_plan()
+    _capi.check("rr_select_plan_from", _capi.lib().rr_select_plan_from(op_id, rows, cols, int(src), p))
+    return p
+
+
+def rr_model_time_us(op, rows, cols, plan) -> float:
+    """The analytic model's predicted microseconds per launch of `plan`
+    (-1.0 for an illegal or split plan)."""
+    op_id = OP_IDS[op] if isinstance(op, str) else int(op)
+    return _capi.lib().rr_model_time_us(op_id, rows, cols, _plan_ptr(plan))
 
 
 def rr_check_plan(op, rows, cols, plan) -> int:

@@ -57,8 +57,12 @@ EXPORTED = (
     "residual_layernorm_bf16_ws", "cross_entropy_bf16_ws",
     "rr_workspace_bytes",
     "rr_select_plan", "rr_check_plan", "rr_status_string",
+    "rr_select_plan_from", "rr_model_time_us",
     "rr_copy_f32", "rr_empty_kernel",
 )
+
+# rr_plan_source
+RR_PLAN_AUTO, RR_PLAN_TABLE, RR_PLAN_MODEL, RR_PLAN_RULE = 0, 1, 2, 3
 
 
 class rr_plan(ctypes.Structure):
@@ -128,6 +132,8 @@ _SIGNATURES = {
     "rr_workspace_bytes": [ctypes.c_int, _i64, _i64, _planp],
     "rr_select_plan": [ctypes.c_int, _i64, _i64, _planp],
     "rr_check_plan": [ctypes.c_int, _i64, _i64, _planp],
+    "rr_select_plan_from": [ctypes.c_int, _i64, _i64, ctypes.c_int, _planp],
+    "rr_model_time_us": [ctypes.c_int, _i64, _i64, _planp],
     "rr_status_string": [ctypes.c_int],
     "rr_copy_f32": [_vp, _vp, _i64, _vp],
     "rr_empty_kernel": [_vp],
@@ -149,7 +155,8 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = argtypes
             fn.restype = {"rr_status_string": ctypes.c_char_p,
-                          "rr_workspace_bytes": ctypes.c_int64}.get(name, ctypes.c_int)
+                          "rr_workspace_bytes": ctypes.c_int64,
+                          "rr_model_time_us": ctypes.c_double}.get(name, ctypes.c_int)
         _lib = L
     return _lib
 

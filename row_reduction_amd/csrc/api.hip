@@ -353,6 +353,14 @@ int rr_check_plan(int op, int64_t rows, int64_t cols, const rr_plan *plan) {
     return check_plan(op, rows, cols, plan);
 }
 
+int rr_select_plan_from(int op, int64_t rows, int64_t cols, int source, rr_plan *out) {
+    return select_plan_from(op, rows, cols, source, out);
+}
+
+double rr_model_time_us(int op, int64_t rows, int64_t cols, const rr_plan *plan) {
+    return model_time_us(op, rows, cols, plan);
+}
+
 int64_t rr_workspace_bytes(int op, int64_t rows, int64_t cols, const rr_plan *plan) {
     rr_plan p;
     if (plan != nullptr) {

@@ -51,5 +51,8 @@ int select_plan(int op, int64_t rows, int64_t cols, rr_plan *out, int max_v = 8,
 int check_plan(int op, int64_t rows, int64_t cols, const rr_plan *plan);
 // Workspace a (legal) plan needs: rows x slices x 16 bytes for split plans, else 0.
 int64_t plan_workspace_bytes(int64_t rows, int64_t cols, const rr_plan *plan);
+// Plan from one source (rr_plan_source); the analytic model's predicted time.
+int select_plan_from(int op, int64_t rows, int64_t cols, int source, rr_plan *out);
+double model_time_us(int op, int64_t rows, int64_t cols, const rr_plan *plan);
 
 }  // namespace rowred

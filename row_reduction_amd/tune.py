@@ -27,6 +27,8 @@ Usage:
   python -m row_reduction_amd.tune --replay search.json --out replay.json
   python -m row_reduction_amd.tune --emit-table replay.json   # writes csrc/plan_table.inc
   python -m row_reduction_amd.tune --summarize search.json replay.json
+  python -m row_reduction_amd.tune --validate --heldout 30 --out validate.json
+  python -m row_reduction_amd.tune --summarize-validate validate.json
 """
 from __future__ import annotations
 
@@ -276,6 +278,92 @@ def run_search(args) -> dict:
     return out
 
 
+def heldout_shapes(n: int, seed: int) -> list[str]:
+    """n seeded (rows, cols) drawn log-uniformly (rows 1..65536, cols
+    32..32768, at most 2^27 elements), none of them a shape the plan table or
+    the model's training timings list."""
+    import random
+    rnd = random.Random(seed)
+    taken = set()
+    for path in (os.path.join(HERE, "data", "plan_timings.csv"),):
+        if os.path.exists(path):
+            import csv
+            taken |= {(int(r["rows"]), int(r["cols"])) for r in csv.DictReader(open(path))}
+    out = []
+    while len(out) < n:
+        rows = int(round(2 ** rnd.uniform(0, 16)))
+        cols = int(round(2 ** rnd.uniform(5, 15)))
+        if rows * cols <= (1 << 27) and (rows, cols) not in taken:
+            taken.add((rows, cols))
+            out.append(f"{rows}x{cols}")
+    return out
+
+
+def run_validate(args) -> dict:
+    """Held-out check of the plan sources: per case, every candidate at the
+    footprint's cache policy plus the exact plans of the analytic model and
+    of the built-in rule, timed together; regret = chosen time / best - 1."""
+    import torch
+    import row_reduction_amd as rr
+    _capi.lib()
+    device = torch.device("cuda:0")
+    out = {"kind": "validate", "source_sha256": source_hash(), "rounds": args.rounds,
+           "samples": args.samples, "cases": []}
+    for op in args.ops:
+        for shape in args.shapes:
+            rows, cols = map(int, shape.split("x"))
+            log(f"validate {op} {shape}")
+            case = Case(torch, op, rows, cols, False, device)
+            caches = (2,) if case.cold else (0,)
+            cands = {plans.plan_key(p): p for p in plans.candidate_plans(op, rows, cols, caches=caches)}
+            chosen = {src: rr.rr_select_plan_from(op, rows, cols, src) for src in ("model", "rule")}
+            for p in chosen.values():
+                cands.setdefault(plans.plan_key(p), p)
+            res = measure(torch, case, cands, args.rounds, args.samples)
+            timed = {k: v["us"] for k, v in res.items() if "us" in v}
+            best = min(timed, key=timed.get)
+            entry = {"op": op, "rows": rows, "cols": cols, "cold": case.cold, "best": best,
+                     "best_us": timed[best], "candidates": {k: round(v, 4) for k, v in timed.items()}}
+            for src, p in chosen.items():
+                k = plans.plan_key(p)
+                entry[src] = k
+                entry[src + "_us"] = timed.get(k)
+                entry[src + "_regret"] = timed[k] / timed[best] - 1.0 if k in timed else None
+            out["cases"].append(entry)
+            log(f"  best {best} {timed[best]:.3f} us; model {entry['model']} regret "
+                f"{entry['model_regret']}; rule {entry['rule']} regret {entry['rule_regret']}")
+            del case
+            torch.cuda.empty_cache()
+    return out
+
+
+def summarize_validate(path: str) -> str:
+    v = json.load(open(path))
+    cs = [c for c in v["cases"] if c.get("model_regret") is not None and c.get("rule_regret") is not None]
+    out = [f"Device source sha256: `{v['source_sha256']}`; {v['rounds']} rounds x {v['samples']} samples; "
+           f"{len(cs)} held-out (operator, shape) cases.", ""]
+
+    def stats(key):
+        r = sorted(c[key] for c in cs)
+        return (statistics.mean(r), statistics.median(r), r[-1], sum(1 for x in r if x > 0.10),
+                sum(1 for x in r if x <= 0.02))
+    out.append("| Plan source | Mean regret | Median | Max | Cases > 10% | Cases within 2% |")
+    out.append("|---|---:|---:|---:|---:|---:|")
+    for src in ("model", "rule"):
+        m, med, mx, over, near = stats(src + "_regret")
+        out.append(f"| {src} | {m:.2%} | {med:.2%} | {mx:.1%} | {over} | {near} |")
+    wins = sum(1 for c in cs if c["model_us"] < c["rule_us"] * 0.98)
+    losses = sum(1 for c in cs if c["rule_us"] < c["model_us"] * 0.98)
+    out += ["", f"Model faster than the rule by > 2%: {wins} cases; rule faster by > 2%: {losses}.", ""]
+    out.append("| Op | Shape | Cache | Best (us) | Model plan (regret) | Rule plan (regret) |")
+    out.append("|---|---|---|---|---|---|")
+    for c in sorted(cs, key=lambda c: (c["op"], c["rows"] * c["cols"])):
+        out.append(f"| {c['op']} | {c['rows']}x{c['cols']} | {'cold' if c['cold'] else 'hot'} | "
+                   f"`{c['best']}` {c['best_us']:.2f} | `{c['model']}` {c['model_regret']:.1%} | "
+                   f"`{c['rule']}` {c['rule_regret']:.1%} |")
+    return "\n".join(out)
+
+
 def run_replay(args) -> dict:
     import torch
     import row_reduction_amd as rr
@@ -394,18 +482,28 @@ def main() -> int:
     ap.add_argument("--emit-table", help="replay result to freeze into plan_table.inc")
     ap.add_argument("--summarize", nargs=2, metavar=("SEARCH", "REPLAY"),
                     help="print a markdown summary of a search and its replay")
+    ap.add_argument("--validate", action="store_true",
+                    help="time every candidate plus the model's and the rule's plans on held-out shapes")
+    ap.add_argument("--heldout", type=int, metavar="N", help="use N seeded held-out shapes")
+    ap.add_argument("--seed", type=int, default=2026)
+    ap.add_argument("--summarize-validate", metavar="VALIDATE_JSON")
     ap.add_argument("--out")
     args = ap.parse_args()
     if args.summarize:
         print(summarize(*args.summarize))
         return 0
+    if args.summarize_validate:
+        print(summarize_validate(args.summarize_validate))
+        return 0
     args.ops = [o for o in args.ops.split(",") if o]
     args.shapes = [s for s in args.shapes.split(",") if s]
+    if args.heldout:
+        args.shapes = heldout_shapes(args.heldout, args.seed)
     if args.emit_table:
         print(emit_table(args.emit_table))
         return 0
     t0 = time.time()
-    res = run_replay(args) if args.replay else run_search(args)
+    res = run_replay(args) if args.replay else (run_validate(args) if args.validate else run_search(args))
     res["elapsed_s"] = time.time() - t0
     text = json.dumps(res)
     if args.out:

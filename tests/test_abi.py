@@ -30,7 +30,7 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int64_t|int|const\s+char\s*\*)\s*(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int64_t|int|double|const\s+char\s*\*)\s*(\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_documented_entry_points():
