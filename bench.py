@@ -17,6 +17,9 @@ eps = 1e-6), inputs resident in HBM. Prints one JSON line:
   shapes     per-shape us/op, rows/s, GB/s and fraction of peak for every
              measured RMSNorm shape and the five sibling operators, next to
              an empty-kernel launch floor and a same-bytes copy ceiling
+  long_rows  few long rows: one workgroup per row against split rows
+  streaming_rows  many rows beyond the register path (vocabulary-size
+             cross-entropy and softmax, 65536-column normalisations)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-shapes] [--no-cpu]
 """
@@ -241,6 +244,34 @@ def long_rows_table(torch, rr, device, samples: int = 11) -> list:
     return out
 
 
+def streaming_table(torch, rr, device, samples: int = 9) -> list:
+    """Rows beyond the register path (vocabulary-size cross-entropy and
+    softmax, 65536-column normalisations), many of them: the streaming plan
+    the selector picks, per call (graph-replayed; every input here is larger
+    than the last-level cache), next to a same-bytes copy."""
+    from row_reduction_amd import workloads
+    from row_reduction_amd.tune import Case, GraphTimer, launches_per_graph
+    out = []
+    cases = [("cross_entropy", 2048, 128256), ("cross_entropy_bf16", 2048, 128256),
+             ("softmax", 2048, 128256), ("softmax_bf16", 2048, 128256),
+             ("rmsnorm", 4096, 65536), ("layernorm", 4096, 65536)]
+    for op, rows, cols in cases:
+        case = Case(torch, op, rows, cols, False, device)
+        plan = rr.rr_select_plan(op, rows, cols)
+        n = launches_per_graph(torch, case, plan)
+        gt = GraphTimer(torch, case, plan, n)
+        vals = sorted(gt.sample_us() for _ in range(samples))
+        us = vals[len(vals) // 2]
+        del gt, case
+        torch.cuda.empty_cache()
+        nbytes = workloads.algorithmic_bytes(op, rows, cols)
+        out.append({"op": op, "shape": f"{rows}x{cols}", "us_per_op": round(us, 3),
+                    "GBps": round(nbytes / (us * 1e3), 1),
+                    "frac_of_peak": round(nbytes / (us * 1e3) / PEAK_HBM_GBPS, 4),
+                    "plan": plan.as_dict()})
+    return out
+
+
 def cpu_baseline(workloads, x_np, w_np, eps, y_gpu_sample, budget_s: float = 10.0) -> dict:
     """The CPU oracle, as it is (plain fp64 C loops), on row blocks of the
     headline input: first on one thread, then on every host core with a
@@ -365,6 +396,7 @@ def main() -> int:
         y_sample = y[:256].cpu().numpy()
     shapes = [] if args.no_shapes else shape_table(torch, rr, workloads, device)
     long_rows = [] if args.no_shapes else long_rows_table(torch, rr, device)
+    streaming = [] if args.no_shapes else streaming_table(torch, rr, device)
 
     result = {
         "metric": METRIC,
@@ -391,6 +423,7 @@ def main() -> int:
         "launch_floor_us": round(empty["us"], 3),
         "shapes": shapes,
         "long_rows": long_rows,
+        "streaming_rows": streaming,
     }
     if not args.no_cpu:
         log(f"cpu baseline ({args.cpu_seconds:.0f} s)")

@@ -40,6 +40,10 @@ def cases_list(shapes_only=None):
     cases += [(op, s) for s in workloads.FAMILY_SHAPES for op in workloads.OPS if op != "rmsnorm"]
     cases += [("rmsnorm_bf16", s) for s in [(1024, 4096), (16384, 8192)]]
     cases += [(op + "_bf16", (1024, 4096)) for op in workloads.OPS if op != "rmsnorm"]
+    # Streaming path: vocabulary-size rows and 65536-column normalisations.
+    cases += [("cross_entropy", (2048, 128256)), ("cross_entropy_bf16", (2048, 128256)),
+              ("softmax", (2048, 128256)), ("softmax_bf16", (2048, 128256)),
+              ("rmsnorm", (4096, 65536)), ("layernorm", (4096, 65536))]
     if shapes_only:
         cases = [c for c in cases if f"{c[1][0]}x{c[1][1]}" in shapes_only]
     return cases
