@@ -20,6 +20,9 @@ eps = 1e-6), inputs resident in HBM. Prints one JSON line:
   long_rows  few long rows: one workgroup per row against split rows
   streaming_rows  many rows beyond the register path (vocabulary-size
              cross-entropy and softmax, 65536-column normalisations)
+  single_call  end-to-end latency of one tiny call (C entry point and
+             binding), and the 24-call operator-coverage set as separate
+             launches against one batched launch
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-shapes] [--no-cpu]
 """
@@ -272,6 +275,139 @@ def streaming_table(torch, rr, device, samples: int = 9) -> list:
     return out
 
 
+def single_call_table(torch, rr, device, reps: int = 200) -> dict:
+    """Latency of tiny calls. (1) One RMSNorm 1x127 call end to end: the C
+    entry point called through ctypes with raw pointers, then the stream
+    synchronised through the HIP runtime, so the figure is the library's
+    launch plus the runtime's round trip (no torch wrapper); and the same
+    through the Python binding. (2) The pages' operator-coverage set (five
+    operators and RMSNorm on four small shapes, 24 calls) as 24 separate
+    launches and as one rr_batch launch: per-set time from HIP-graph replay
+    (GPU side) and end to end with one synchronisation."""
+    import ctypes
+    import statistics
+
+    from row_reduction_amd import _capi, workloads
+    L = _capi.lib()
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        hip = ctypes.CDLL(os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib", "libamdhip64.so"))
+    hip.hipStreamSynchronize.argtypes = [ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    x = torch.randn(1, 127, device=device)
+    w = torch.rand(127, device=device) + 0.5
+    y = torch.empty_like(x)
+    xp, wp, yp = x.data_ptr(), w.data_ptr(), y.data_ptr()
+
+    def e2e(fn, n):
+        out = []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            fn()
+            out.append((time.perf_counter() - t0) * 1e6)
+        return statistics.median(out)
+
+    def native():
+        L.rmsnorm_f32(xp, wp, yp, 1, 127, 1e-6, stream)
+        hip.hipStreamSynchronize(stream)
+
+    def binding():
+        rr.rmsnorm_f32(x, w, 1e-6, y=y)
+        torch.cuda.synchronize()
+    for _ in range(20):
+        native()
+        binding()
+    res = {"rmsnorm_1x127_native_us": round(e2e(native, reps), 2),
+           "rmsnorm_1x127_binding_us": round(e2e(binding, reps), 2)}
+
+    # The operator-coverage set, 24 problems.
+    probs, calls, ccalls = [], [], []
+    keep = []
+    for i, (rows, cols) in enumerate(workloads.FAMILY_SHAPES):
+        d = workloads.family_inputs(rows, cols, 700 + i)
+        t = {k: torch.from_numpy(v).to(device) for k, v in d.items()}
+        keep.append(t)
+        for op in workloads.OPS:
+            kw = {}
+            if op in ("rmsnorm", "layernorm", "residual_layernorm"):
+                kw.update(w=t["gamma"], eps=1e-6 if op == "rmsnorm" else 1e-5)
+            if op in ("layernorm", "residual_layernorm"):
+                kw["beta"] = t["beta"]
+            if op == "residual_layernorm":
+                kw["residual"] = t["residual"]
+            if op == "cross_entropy":
+                kw["targets"] = t["targets"]
+            p, outs = rr.batch_problem(op, t["x"], **kw)
+            probs.append(p)
+            keep.append(outs)
+
+            xp_, op_ = t["x"].data_ptr(), op
+            rows_, cols_ = t["x"].shape
+            if op == "rmsnorm":
+                args = (xp_, t["gamma"].data_ptr(), outs["y"].data_ptr(), rows_, cols_, 1e-6)
+            elif op == "sum":
+                args = (xp_, outs["out"].data_ptr(), rows_, cols_)
+            elif op == "softmax":
+                args = (xp_, outs["y"].data_ptr(), rows_, cols_)
+            elif op == "layernorm":
+                args = (xp_, t["gamma"].data_ptr(), t["beta"].data_ptr(), outs["y"].data_ptr(), rows_, cols_, 1e-5)
+            elif op == "residual_layernorm":
+                args = (xp_, t["residual"].data_ptr(), t["gamma"].data_ptr(), t["beta"].data_ptr(),
+                        outs["y"].data_ptr(), None, rows_, cols_, 1e-5)
+            else:
+                args = (xp_, t["targets"].data_ptr(), outs["out"].data_ptr(), rows_, cols_)
+            ccalls.append((getattr(L, {"sum": "row_sum"}.get(op_, op_) + "_f32"), args))
+
+            def call(op=op, t=t, kw=kw, outs=outs):
+                if op == "rmsnorm":
+                    rr.rmsnorm_f32(t["x"], kw["w"], kw["eps"], y=outs["y"])
+                elif op == "sum":
+                    rr.row_sum_f32(t["x"], out=outs["out"])
+                elif op == "softmax":
+                    rr.softmax_f32(t["x"], y=outs["y"])
+                elif op == "layernorm":
+                    rr.layernorm_f32(t["x"], kw["w"], kw["beta"], kw["eps"], y=outs["y"])
+                elif op == "residual_layernorm":
+                    rr.residual_layernorm_f32(t["x"], kw["residual"], kw["w"], kw["beta"], kw["eps"], y=outs["y"])
+                else:
+                    rr.cross_entropy_f32(t["x"], kw["targets"], loss=outs["out"])
+            calls.append(call)
+    arr = (_capi.rr_problem * len(probs))(*probs)
+
+    def separate():
+        for c in calls:
+            c()
+
+    def batched():
+        st = L.rr_batch(arr, len(probs), torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"rr_batch failed: {st}")
+
+    def separate_c():
+        for fn, args in ccalls:
+            fn(*args, stream)
+    sep = graph_us(torch, separate, 20)
+    bat = graph_us(torch, batched, 20)
+
+    def sync(fn):
+        def f():
+            fn()
+            hip.hipStreamSynchronize(stream)
+        return f
+    for _ in range(10):
+        sync(separate)()
+        sync(separate_c)()
+        sync(batched)()
+    res.update({"coverage_set_problems": len(probs),
+                "coverage_set_separate_gpu_us": round(sep["us"], 2),
+                "coverage_set_batched_gpu_us": round(bat["us"], 2),
+                "coverage_set_separate_binding_e2e_us": round(e2e(sync(separate), 50), 2),
+                "coverage_set_separate_c_e2e_us": round(e2e(sync(separate_c), 50), 2),
+                "coverage_set_batched_c_e2e_us": round(e2e(sync(batched), reps), 2)})
+    return res
+
+
 def cpu_baseline(workloads, x_np, w_np, eps, y_gpu_sample, budget_s: float = 10.0) -> dict:
     """The CPU oracle, as it is (plain fp64 C loops), on row blocks of the
     headline input: first on one thread, then on every host core with a
@@ -397,6 +533,7 @@ def main() -> int:
     shapes = [] if args.no_shapes else shape_table(torch, rr, workloads, device)
     long_rows = [] if args.no_shapes else long_rows_table(torch, rr, device)
     streaming = [] if args.no_shapes else streaming_table(torch, rr, device)
+    single = {} if args.no_shapes else single_call_table(torch, rr, device)
 
     result = {
         "metric": METRIC,
@@ -424,6 +561,7 @@ def main() -> int:
         "shapes": shapes,
         "long_rows": long_rows,
         "streaming_rows": streaming,
+        "single_call": single,
     }
     if not args.no_cpu:
         log(f"cpu baseline ({args.cpu_seconds:.0f} s)")

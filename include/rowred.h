@@ -279,6 +279,46 @@ int cross_entropy_bf16_ws(const uint16_t *logits, const int32_t *targets, float 
                           int64_t rows, int64_t cols,
                           const rr_plan *plan, void *workspace, int64_t workspace_bytes, void *stream);
 
+/* ---- Batched launch -------------------------------------------------------
+ * Many small independent problems in one kernel launch, so that a sequence
+ * of tiny operator calls pays one launch instead of one each (the per-launch
+ * cost dominates below about 100 KB per call). Meant for small problems:
+ * every row takes one 64-lane wavefront on the streaming row body (one pass
+ * for statistics, one for outputs), which is slower than the operator's own
+ * entry point for large rows. */
+
+#define RR_BATCH_MAX 32
+
+/* One problem of a batch: op is an rr_op (float or bfloat16 storage); the
+ * pointers mean what they mean in that operator's entry point (x = logits
+ * for cross-entropy, w = gamma for the LayerNorms, row_out = row sum `out`
+ * or cross-entropy `loss`); fields the operator does not use are ignored. */
+typedef struct rr_problem {
+    int32_t op;
+    float eps;
+    int64_t rows;
+    int64_t cols;
+    const void *x;
+    const void *residual;
+    const void *w;
+    const void *beta;
+    const int32_t *targets;
+    void *y;
+    void *h_out;
+    float *row_out;
+} rr_problem;
+
+/* Runs problems[0 .. count-1] (0 <= count <= RR_BATCH_MAX) with one kernel
+ * launch on `stream`; each problem's results equal its operator's (to the
+ * same tolerance against the exact values; the reduction order differs).
+ * Every problem is validated as its entry point would validate it before
+ * anything is launched: any invalid problem fails the whole batch with that
+ * entry point's status. Problems with rows == 0 are skipped; more than
+ * 2^31-1 rows in total give RR_ERR_UNSUPPORTED. Problems must not write to
+ * memory another problem of the batch reads or writes (they run
+ * concurrently). The problems array is read during the call only. */
+int rr_batch(const rr_problem *problems, int32_t count, void *stream);
+
 /* Plan the library would use for (op, rows, cols): the measured per-shape
  * table entry when one exists, else the analytic model's cheapest legal
  * candidate (see rr_model_time_us). Pure host function; no GPU needed.

@@ -22,7 +22,7 @@ __all__ = [
     "residual_layernorm_bf16", "cross_entropy_bf16",
     "rr_select_plan", "rr_select_plan_from", "rr_model_time_us", "rr_check_plan", "rr_status_string",
     "rr_copy_f32", "rr_empty_kernel",
-    "rr_workspace_bytes", "workspace_for",
+    "rr_workspace_bytes", "workspace_for", "batch_problem", "rr_batch",
     "rr_plan", "RowRedError", "OP_IDS",
 ]
 
@@ -288,6 +288,59 @@ def rr_select_plan(op, rows, cols) -> rr_plan:
     p = rr_plan()
     _capi.check("rr_select_plan", _capi.lib().rr_select_plan(op_id, rows, cols, p))
     return p
+
+
+def batch_problem(op, x, w=None, beta=None, residual=None, targets=None, eps=None, y=None, h_out=None,
+                  out=None):
+    """One problem for rr_batch on torch tensors: `op` is an operator name
+    ("rmsnorm", "layernorm_bf16", ...); w is RMSNorm's w or LayerNorm's
+    gamma; outputs not given are allocated. Returns (rr_problem, outputs)
+    where outputs maps "y", "h" or "out" to the tensors the call writes; the
+    caller keeps every tensor alive until the batch has run."""
+    torch = _torch()
+    bf = op.endswith("_bf16")
+    base = op[:-5] if bf else op
+    if base not in ("rmsnorm", "sum", "softmax", "layernorm", "residual_layernorm", "cross_entropy"):
+        raise ValueError(f"unknown operator {op!r}")
+    dt = _bf16() if bf else torch.float32
+    _mat(x, "x", dt)
+    rows, cols = x.shape
+    p = _capi.rr_problem()
+    p.op, p.rows, p.cols, p.x = OP_IDS[op], rows, cols, x.data_ptr()
+    outs = {}
+    if base in ("rmsnorm", "layernorm", "residual_layernorm"):
+        _vec(w, cols, "w", dt)
+        p.w = w.data_ptr()
+        p.eps = float(eps if eps is not None else (1e-6 if base == "rmsnorm" else 1e-5))
+    if base in ("layernorm", "residual_layernorm"):
+        _vec(beta, cols, "beta", dt)
+        p.beta = beta.data_ptr()
+    if base == "residual_layernorm":
+        _mat(residual, "residual", dt)
+        if residual.shape != x.shape:
+            raise ValueError("residual must have the shape of x")
+        p.residual = residual.data_ptr()
+        if h_out is not None:
+            outs["h"] = _out_like(h_out, x, "h_out")
+            p.h_out = h_out.data_ptr()
+    if base == "cross_entropy":
+        if not isinstance(targets, torch.Tensor) or targets.dtype != torch.int32 or not targets.is_cuda \
+                or targets.shape != (rows,) or not targets.is_contiguous():
+            raise TypeError("targets must be a contiguous int32 CUDA/HIP tensor of shape (rows,)")
+        p.targets = targets.data_ptr()
+    if base in ("sum", "cross_entropy"):
+        outs["out"] = _out_rows(out, x, "out")
+        p.row_out = outs["out"].data_ptr()
+    else:
+        outs["y"] = _out_like(y, x, "y")
+        p.y = outs["y"].data_ptr()
+    return p, outs
+
+
+def rr_batch(problems, stream=None) -> None:
+    """Run up to RR_BATCH_MAX problems (from batch_problem) in one kernel launch."""
+    arr = (_capi.rr_problem * max(1, len(problems)))(*problems)
+    _capi.check("rr_batch", _capi.lib().rr_batch(arr, len(problems), _stream(stream)))
 
 
 def rr_select_plan_from(op, rows, cols, source) -> rr_plan:

@@ -57,7 +57,7 @@ EXPORTED = (
     "residual_layernorm_bf16_ws", "cross_entropy_bf16_ws",
     "rr_workspace_bytes",
     "rr_select_plan", "rr_check_plan", "rr_status_string",
-    "rr_select_plan_from", "rr_model_time_us",
+    "rr_select_plan_from", "rr_model_time_us", "rr_batch",
     "rr_copy_f32", "rr_empty_kernel",
 )
 
@@ -91,6 +91,27 @@ _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _f32 = ctypes.c_float
 _planp = ctypes.POINTER(rr_plan)
+
+RR_BATCH_MAX = 32
+
+
+class rr_problem(ctypes.Structure):
+    """One problem of rr_batch (include/rowred.h)."""
+    _fields_ = [
+        ("op", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("x", ctypes.c_void_p),
+        ("residual", ctypes.c_void_p),
+        ("w", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p),
+        ("targets", ctypes.c_void_p),
+        ("y", ctypes.c_void_p),
+        ("h_out", ctypes.c_void_p),
+        ("row_out", ctypes.c_void_p),
+    ]
+
 
 _SIGNATURES = {
     "rmsnorm_f32": [_vp, _vp, _vp, _i64, _i64, _f32, _vp],
@@ -134,6 +155,7 @@ _SIGNATURES = {
     "rr_check_plan": [ctypes.c_int, _i64, _i64, _planp],
     "rr_select_plan_from": [ctypes.c_int, _i64, _i64, ctypes.c_int, _planp],
     "rr_model_time_us": [ctypes.c_int, _i64, _i64, _planp],
+    "rr_batch": [ctypes.POINTER(rr_problem), ctypes.c_int32, _vp],
     "rr_status_string": [ctypes.c_int],
     "rr_copy_f32": [_vp, _vp, _i64, _vp],
     "rr_empty_kernel": [_vp],

@@ -39,6 +39,7 @@ HIP_SOURCES = [
     "kernels_layernorm_bf16.hip",
     "kernels_residual_layernorm_bf16.hip",
     "kernels_cross_entropy_bf16.hip",
+    "kernels_batch.hip",
 ]
 CXX_SOURCES = ["plan.cpp"]
 

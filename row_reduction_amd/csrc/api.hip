@@ -86,80 +86,142 @@ Args base_args(int64_t rows, int64_t cols) {
     return a;
 }
 
-// Per-operator front ends shared by the float and bfloat16 entry points;
-// E is the element size of the row and weight tensors.
-int rmsnorm_call(int op, uintptr_t E, const void *x, const void *w, void *y, int64_t rows, int64_t cols,
-                 float eps, const rr_plan *plan, void *ws, int64_t wsb, void *stream) {
-    int st = check_shape(rows, cols);
+// The operands of one operator call, as the entry points and rr_batch get them.
+struct Operands {
+    const void *x = nullptr, *residual = nullptr, *w = nullptr, *beta = nullptr;
+    const int32_t *targets = nullptr;
+    void *y = nullptr, *h_out = nullptr;
+    float *row_out = nullptr;
+    int64_t rows = 0, cols = 0;
+    float eps = 0.0f;
+};
+
+// Validation shared by every entry point and rr_batch: shape first; with
+// rows == 0 nothing is read or written and the pointers are not looked at;
+// else every required pointer present and aligned to its element size (E =
+// 2 for bfloat16 rows and weights, 4 for float; int32 targets and float
+// per-row outputs 4), optional ones null or aligned, eps finite and >= 0.
+// Fills the kernel arguments and the widest bfloat16 pack the pointers'
+// alignment allows.
+int prepare(int op, const Operands &o, Args *a, int *max_v) {
+    const int st = check_shape(o.rows, o.cols);
     if (st != RR_OK) return st;
-    if (rows == 0) return RR_OK;
-    if (!ok_ptr(x, E) || !ok_ptr(w, E) || !ok_ptr(y, E) || !ok_eps(eps)) return RR_ERR_INVALID_ARGUMENT;
-    Args a = base_args(rows, cols);
-    a.x = x;
-    a.w = w;
-    a.y = y;
-    a.eps = eps;
-    return run(op, a, plan, ws, wsb, bf16_op(op) ? max_v_for({x, w, y}) : 8, stream);
+    *a = base_args(o.rows, o.cols);
+    *max_v = 8;
+    if (o.rows == 0) return RR_OK;
+    const bool bf = bf16_op(op);
+    const uintptr_t E = bf ? 2 : 4;
+    switch (bf ? op - RR_OP_RMSNORM_BF16 : op) {
+        case RR_OP_RMSNORM:
+            if (!ok_ptr(o.x, E) || !ok_ptr(o.w, E) || !ok_ptr(o.y, E) || !ok_eps(o.eps))
+                return RR_ERR_INVALID_ARGUMENT;
+            if (bf) *max_v = max_v_for({o.x, o.w, o.y});
+            break;
+        case RR_OP_SUM:
+            if (!ok_ptr(o.x, E) || !ok_ptr(o.row_out, 4)) return RR_ERR_INVALID_ARGUMENT;
+            if (bf) *max_v = max_v_for({o.x});
+            break;
+        case RR_OP_SOFTMAX:
+            if (!ok_ptr(o.x, E) || !ok_ptr(o.y, E)) return RR_ERR_INVALID_ARGUMENT;
+            if (bf) *max_v = max_v_for({o.x, o.y});
+            break;
+        case RR_OP_LAYERNORM:
+        case RR_OP_RESIDUAL_LAYERNORM: {
+            const bool residual_op = (op == RR_OP_RESIDUAL_LAYERNORM || op == RR_OP_RESIDUAL_LAYERNORM_BF16);
+            if (!ok_ptr(o.x, E) || !ok_ptr(o.w, E) || !ok_ptr(o.beta, E) || !ok_ptr(o.y, E) ||
+                !ok_eps(o.eps) || (residual_op && !ok_ptr(o.residual, E)) || !ok_opt(o.h_out, E))
+                return RR_ERR_INVALID_ARGUMENT;
+            if (bf) *max_v = max_v_for({o.x, o.residual, o.w, o.beta, o.y, o.h_out});
+            break;
+        }
+        case RR_OP_CROSS_ENTROPY:
+            if (!ok_ptr(o.x, E) || !ok_ptr(o.targets, 4) || !ok_ptr(o.row_out, 4))
+                return RR_ERR_INVALID_ARGUMENT;
+            if (bf) *max_v = max_v_for({o.x});
+            break;
+        default:
+            return RR_ERR_INVALID_ARGUMENT;
+    }
+    // Only the operands the operator uses reach the kernel.
+    const int base = bf ? op - RR_OP_RMSNORM_BF16 : op;
+    a->x = o.x;
+    if (base == RR_OP_RESIDUAL_LAYERNORM) a->residual = o.residual;
+    if (base == RR_OP_RMSNORM || base == RR_OP_LAYERNORM || base == RR_OP_RESIDUAL_LAYERNORM) a->w = o.w;
+    if (base == RR_OP_LAYERNORM || base == RR_OP_RESIDUAL_LAYERNORM) a->beta = o.beta;
+    if (base == RR_OP_CROSS_ENTROPY) a->targets = o.targets;
+    if (base != RR_OP_SUM && base != RR_OP_CROSS_ENTROPY) a->y = o.y;
+    if (base == RR_OP_RESIDUAL_LAYERNORM) a->h_out = o.h_out;
+    if (base == RR_OP_SUM || base == RR_OP_CROSS_ENTROPY) a->row_out = o.row_out;
+    if (base == RR_OP_RMSNORM || base == RR_OP_LAYERNORM || base == RR_OP_RESIDUAL_LAYERNORM) a->eps = o.eps;
+    return RR_OK;
 }
 
-int row_sum_call(int op, uintptr_t E, const void *x, float *out, int64_t rows, int64_t cols,
+int call_op(int op, const Operands &o, const rr_plan *plan, void *ws, int64_t wsb, void *stream) {
+    Args a;
+    int max_v;
+    const int st = prepare(op, o, &a, &max_v);
+    if (st != RR_OK || o.rows == 0) return st;
+    return run(op, a, plan, ws, wsb, max_v, stream);
+}
+
+// Per-operator front ends shared by the float and bfloat16 entry points.
+int rmsnorm_call(int op, const void *x, const void *w, void *y, int64_t rows, int64_t cols, float eps,
                  const rr_plan *plan, void *ws, int64_t wsb, void *stream) {
-    int st = check_shape(rows, cols);
-    if (st != RR_OK) return st;
-    if (rows == 0) return RR_OK;
-    if (!ok_ptr(x, E) || !ok_ptr(out, 4)) return RR_ERR_INVALID_ARGUMENT;
-    Args a = base_args(rows, cols);
-    a.x = x;
-    a.row_out = out;
-    return run(op, a, plan, ws, wsb, bf16_op(op) ? max_v_for({x}) : 8, stream);
+    Operands o;
+    o.x = x;
+    o.w = w;
+    o.y = y;
+    o.rows = rows;
+    o.cols = cols;
+    o.eps = eps;
+    return call_op(op, o, plan, ws, wsb, stream);
 }
 
-int softmax_call(int op, uintptr_t E, const void *x, void *y, int64_t rows, int64_t cols,
-                 const rr_plan *plan, void *ws, int64_t wsb, void *stream) {
-    int st = check_shape(rows, cols);
-    if (st != RR_OK) return st;
-    if (rows == 0) return RR_OK;
-    if (!ok_ptr(x, E) || !ok_ptr(y, E)) return RR_ERR_INVALID_ARGUMENT;
-    Args a = base_args(rows, cols);
-    a.x = x;
-    a.y = y;
-    return run(op, a, plan, ws, wsb, bf16_op(op) ? max_v_for({x, y}) : 8, stream);
+int row_sum_call(int op, const void *x, float *out, int64_t rows, int64_t cols, const rr_plan *plan,
+                 void *ws, int64_t wsb, void *stream) {
+    Operands o;
+    o.x = x;
+    o.row_out = out;
+    o.rows = rows;
+    o.cols = cols;
+    return call_op(op, o, plan, ws, wsb, stream);
 }
 
-int layernorm_call(int op, uintptr_t E, const void *x, const void *residual, const void *gamma,
-                   const void *beta, void *y, void *h_out, int64_t rows, int64_t cols, float eps,
-                   const rr_plan *plan, void *ws, int64_t wsb, void *stream) {
-    int st = check_shape(rows, cols);
-    if (st != RR_OK) return st;
-    if (rows == 0) return RR_OK;
-    const bool residual_op = (op == RR_OP_RESIDUAL_LAYERNORM || op == RR_OP_RESIDUAL_LAYERNORM_BF16);
-    if (!ok_ptr(x, E) || !ok_ptr(gamma, E) || !ok_ptr(beta, E) || !ok_ptr(y, E) || !ok_eps(eps) ||
-        (residual_op && !ok_ptr(residual, E)) || !ok_opt(h_out, E))
-        return RR_ERR_INVALID_ARGUMENT;
-    Args a = base_args(rows, cols);
-    a.x = x;
-    a.residual = residual;
-    a.w = gamma;
-    a.beta = beta;
-    a.y = y;
-    a.h_out = h_out;
-    a.eps = eps;
-    return run(op, a, plan, ws, wsb, bf16_op(op) ? max_v_for({x, residual, gamma, beta, y, h_out}) : 8,
-               stream);
+int softmax_call(int op, const void *x, void *y, int64_t rows, int64_t cols, const rr_plan *plan, void *ws,
+                 int64_t wsb, void *stream) {
+    Operands o;
+    o.x = x;
+    o.y = y;
+    o.rows = rows;
+    o.cols = cols;
+    return call_op(op, o, plan, ws, wsb, stream);
 }
 
-int cross_entropy_call(int op, uintptr_t E, const void *logits, const int32_t *targets, float *loss,
-                       int64_t rows, int64_t cols, const rr_plan *plan, void *ws, int64_t wsb,
-                       void *stream) {
-    int st = check_shape(rows, cols);
-    if (st != RR_OK) return st;
-    if (rows == 0) return RR_OK;
-    if (!ok_ptr(logits, E) || !ok_ptr(targets, 4) || !ok_ptr(loss, 4)) return RR_ERR_INVALID_ARGUMENT;
-    Args a = base_args(rows, cols);
-    a.x = logits;
-    a.targets = targets;
-    a.row_out = loss;
-    return run(op, a, plan, ws, wsb, bf16_op(op) ? max_v_for({logits}) : 8, stream);
+int layernorm_call(int op, const void *x, const void *residual, const void *gamma, const void *beta, void *y,
+                   void *h_out, int64_t rows, int64_t cols, float eps, const rr_plan *plan, void *ws,
+                   int64_t wsb, void *stream) {
+    Operands o;
+    o.x = x;
+    o.residual = residual;
+    o.w = gamma;
+    o.beta = beta;
+    o.y = y;
+    o.h_out = h_out;
+    o.rows = rows;
+    o.cols = cols;
+    o.eps = eps;
+    return call_op(op, o, plan, ws, wsb, stream);
+}
+
+int cross_entropy_call(int op, const void *logits, const int32_t *targets, float *loss, int64_t rows,
+                       int64_t cols, const rr_plan *plan, void *ws, int64_t wsb, void *stream) {
+    Operands o;
+    o.x = logits;
+    o.targets = targets;
+    o.row_out = loss;
+    o.rows = rows;
+    o.cols = cols;
+    return call_op(op, o, plan, ws, wsb, stream);
 }
 
 }  // namespace
@@ -173,7 +235,7 @@ extern "C" {
 
 int rmsnorm_f32_ws(const float *x, const float *w, float *y, int64_t rows, int64_t cols, float eps,
                    const rr_plan *plan, void *ws, int64_t wsb, void *stream) {
-    return rmsnorm_call(RR_OP_RMSNORM, 4, x, w, y, rows, cols, eps, plan, ws, wsb, stream);
+    return rmsnorm_call(RR_OP_RMSNORM, x, w, y, rows, cols, eps, plan, ws, wsb, stream);
 }
 int rmsnorm_f32_ex(const float *x, const float *w, float *y, int64_t rows, int64_t cols, float eps,
                    const rr_plan *plan, void *stream) {
@@ -186,7 +248,7 @@ int rmsnorm_f32(const float *x, const float *w, float *y, int64_t rows, int64_t 
 
 int row_sum_f32_ws(const float *x, float *out, int64_t rows, int64_t cols, const rr_plan *plan, void *ws,
                    int64_t wsb, void *stream) {
-    return row_sum_call(RR_OP_SUM, 4, x, out, rows, cols, plan, ws, wsb, stream);
+    return row_sum_call(RR_OP_SUM, x, out, rows, cols, plan, ws, wsb, stream);
 }
 int row_sum_f32_ex(const float *x, float *out, int64_t rows, int64_t cols, const rr_plan *plan,
                    void *stream) {
@@ -198,7 +260,7 @@ int row_sum_f32(const float *x, float *out, int64_t rows, int64_t cols, void *st
 
 int softmax_f32_ws(const float *x, float *y, int64_t rows, int64_t cols, const rr_plan *plan, void *ws,
                    int64_t wsb, void *stream) {
-    return softmax_call(RR_OP_SOFTMAX, 4, x, y, rows, cols, plan, ws, wsb, stream);
+    return softmax_call(RR_OP_SOFTMAX, x, y, rows, cols, plan, ws, wsb, stream);
 }
 int softmax_f32_ex(const float *x, float *y, int64_t rows, int64_t cols, const rr_plan *plan,
                    void *stream) {
@@ -210,7 +272,7 @@ int softmax_f32(const float *x, float *y, int64_t rows, int64_t cols, void *stre
 
 int layernorm_f32_ws(const float *x, const float *gamma, const float *beta, float *y, int64_t rows,
                      int64_t cols, float eps, const rr_plan *plan, void *ws, int64_t wsb, void *stream) {
-    return layernorm_call(RR_OP_LAYERNORM, 4, x, nullptr, gamma, beta, y, nullptr, rows, cols, eps, plan,
+    return layernorm_call(RR_OP_LAYERNORM, x, nullptr, gamma, beta, y, nullptr, rows, cols, eps, plan,
                           ws, wsb, stream);
 }
 int layernorm_f32_ex(const float *x, const float *gamma, const float *beta, float *y, int64_t rows,
@@ -225,7 +287,7 @@ int layernorm_f32(const float *x, const float *gamma, const float *beta, float *
 int residual_layernorm_f32_ws(const float *x, const float *residual, const float *gamma,
                               const float *beta, float *y, float *h_out, int64_t rows, int64_t cols,
                               float eps, const rr_plan *plan, void *ws, int64_t wsb, void *stream) {
-    return layernorm_call(RR_OP_RESIDUAL_LAYERNORM, 4, x, residual, gamma, beta, y, h_out, rows, cols, eps,
+    return layernorm_call(RR_OP_RESIDUAL_LAYERNORM, x, residual, gamma, beta, y, h_out, rows, cols, eps,
                           plan, ws, wsb, stream);
 }
 int residual_layernorm_f32_ex(const float *x, const float *residual, const float *gamma,
@@ -243,7 +305,7 @@ int residual_layernorm_f32(const float *x, const float *residual, const float *g
 
 int cross_entropy_f32_ws(const float *logits, const int32_t *targets, float *loss, int64_t rows,
                          int64_t cols, const rr_plan *plan, void *ws, int64_t wsb, void *stream) {
-    return cross_entropy_call(RR_OP_CROSS_ENTROPY, 4, logits, targets, loss, rows, cols, plan, ws, wsb,
+    return cross_entropy_call(RR_OP_CROSS_ENTROPY, logits, targets, loss, rows, cols, plan, ws, wsb,
                               stream);
 }
 int cross_entropy_f32_ex(const float *logits, const int32_t *targets, float *loss, int64_t rows,
@@ -259,7 +321,7 @@ int cross_entropy_f32(const float *logits, const int32_t *targets, float *loss, 
 
 int rmsnorm_bf16_ws(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t rows, int64_t cols,
                     float eps, const rr_plan *plan, void *ws, int64_t wsb, void *stream) {
-    return rmsnorm_call(RR_OP_RMSNORM_BF16, 2, x, w, y, rows, cols, eps, plan, ws, wsb, stream);
+    return rmsnorm_call(RR_OP_RMSNORM_BF16, x, w, y, rows, cols, eps, plan, ws, wsb, stream);
 }
 int rmsnorm_bf16_ex(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t rows, int64_t cols,
                     float eps, const rr_plan *plan, void *stream) {
@@ -272,7 +334,7 @@ int rmsnorm_bf16(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t rows
 
 int row_sum_bf16_ws(const uint16_t *x, float *out, int64_t rows, int64_t cols, const rr_plan *plan,
                     void *ws, int64_t wsb, void *stream) {
-    return row_sum_call(RR_OP_SUM_BF16, 2, x, out, rows, cols, plan, ws, wsb, stream);
+    return row_sum_call(RR_OP_SUM_BF16, x, out, rows, cols, plan, ws, wsb, stream);
 }
 int row_sum_bf16_ex(const uint16_t *x, float *out, int64_t rows, int64_t cols, const rr_plan *plan,
                     void *stream) {
@@ -284,7 +346,7 @@ int row_sum_bf16(const uint16_t *x, float *out, int64_t rows, int64_t cols, void
 
 int softmax_bf16_ws(const uint16_t *x, uint16_t *y, int64_t rows, int64_t cols, const rr_plan *plan,
                     void *ws, int64_t wsb, void *stream) {
-    return softmax_call(RR_OP_SOFTMAX_BF16, 2, x, y, rows, cols, plan, ws, wsb, stream);
+    return softmax_call(RR_OP_SOFTMAX_BF16, x, y, rows, cols, plan, ws, wsb, stream);
 }
 int softmax_bf16_ex(const uint16_t *x, uint16_t *y, int64_t rows, int64_t cols, const rr_plan *plan,
                     void *stream) {
@@ -297,7 +359,7 @@ int softmax_bf16(const uint16_t *x, uint16_t *y, int64_t rows, int64_t cols, voi
 int layernorm_bf16_ws(const uint16_t *x, const uint16_t *gamma, const uint16_t *beta, uint16_t *y,
                       int64_t rows, int64_t cols, float eps, const rr_plan *plan, void *ws, int64_t wsb,
                       void *stream) {
-    return layernorm_call(RR_OP_LAYERNORM_BF16, 2, x, nullptr, gamma, beta, y, nullptr, rows, cols, eps,
+    return layernorm_call(RR_OP_LAYERNORM_BF16, x, nullptr, gamma, beta, y, nullptr, rows, cols, eps,
                           plan, ws, wsb, stream);
 }
 int layernorm_bf16_ex(const uint16_t *x, const uint16_t *gamma, const uint16_t *beta, uint16_t *y,
@@ -313,7 +375,7 @@ int residual_layernorm_bf16_ws(const uint16_t *x, const uint16_t *residual, cons
                                const uint16_t *beta, uint16_t *y, uint16_t *h_out, int64_t rows,
                                int64_t cols, float eps, const rr_plan *plan, void *ws, int64_t wsb,
                                void *stream) {
-    return layernorm_call(RR_OP_RESIDUAL_LAYERNORM_BF16, 2, x, residual, gamma, beta, y, h_out, rows, cols,
+    return layernorm_call(RR_OP_RESIDUAL_LAYERNORM_BF16, x, residual, gamma, beta, y, h_out, rows, cols,
                           eps, plan, ws, wsb, stream);
 }
 int residual_layernorm_bf16_ex(const uint16_t *x, const uint16_t *residual, const uint16_t *gamma,
@@ -331,7 +393,7 @@ int residual_layernorm_bf16(const uint16_t *x, const uint16_t *residual, const u
 
 int cross_entropy_bf16_ws(const uint16_t *logits, const int32_t *targets, float *loss, int64_t rows,
                           int64_t cols, const rr_plan *plan, void *ws, int64_t wsb, void *stream) {
-    return cross_entropy_call(RR_OP_CROSS_ENTROPY_BF16, 2, logits, targets, loss, rows, cols, plan, ws,
+    return cross_entropy_call(RR_OP_CROSS_ENTROPY_BF16, logits, targets, loss, rows, cols, plan, ws,
                               wsb, stream);
 }
 int cross_entropy_bf16_ex(const uint16_t *logits, const int32_t *targets, float *loss, int64_t rows,
@@ -351,6 +413,53 @@ int rr_select_plan(int op, int64_t rows, int64_t cols, rr_plan *out) {
 
 int rr_check_plan(int op, int64_t rows, int64_t cols, const rr_plan *plan) {
     return check_plan(op, rows, cols, plan);
+}
+
+int rr_batch(const rr_problem *problems, int32_t count, void *stream) {
+    if (count < 0 || count > RR_BATCH_MAX || (count > 0 && problems == nullptr)) return RR_ERR_INVALID_ARGUMENT;
+    BatchArgs b = {};
+    int n = 0;
+    int64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        const rr_problem &q = problems[i];
+        Operands o;
+        o.x = q.x;
+        o.residual = q.residual;
+        o.w = q.w;
+        o.beta = q.beta;
+        o.targets = q.targets;
+        o.y = q.y;
+        o.h_out = q.h_out;
+        o.row_out = q.row_out;
+        o.rows = q.rows;
+        o.cols = q.cols;
+        o.eps = q.eps;
+        Args a;
+        int max_v;
+        const int st = prepare(q.op, o, &a, &max_v);
+        if (st != RR_OK) return st;
+        if (q.rows == 0) continue;
+        const bool wide = bf16_op(q.op) ? (max_v >= 8 && q.cols % 8 == 0) : q.cols >= 4;
+        BatchProblem &p = b.p[n++];
+        p.x = a.x;
+        p.residual = a.residual;
+        p.w = a.w;
+        p.beta = a.beta;
+        p.targets = a.targets;
+        p.y = a.y;
+        p.h_out = a.h_out;
+        p.row_out = a.row_out;
+        p.rows = a.rows;
+        p.first_block = blocks;
+        p.cols = a.cols;
+        p.variant = 2 * q.op + (wide ? 1 : 0);
+        p.eps = a.eps;
+        blocks += a.rows;
+    }
+    if (blocks > 0x7fffffff) return RR_ERR_UNSUPPORTED;
+    if (n == 0) return RR_OK;
+    b.count = n;
+    return launch_batch(b, blocks, stream) == (int)hipSuccess ? RR_OK : RR_ERR_LAUNCH;
 }
 
 int rr_select_plan_from(int op, int64_t rows, int64_t cols, int source, rr_plan *out) {

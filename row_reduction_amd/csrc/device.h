@@ -555,7 +555,7 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
 // bounds (a pack past the row end reads the row's last window and keeps none
 // of it).
 template <int OP, int V, int KEEP, int HINT, class T>
-__global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
+__device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
     const T *Wt = static_cast<const T *>(a.w);
     const T *B = static_cast<const T *>(a.beta);
     T *Y = static_cast<T *>(a.y);
@@ -564,7 +564,6 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
     __shared__ double ldsd[16];
     const RowLanes<64> rl(a);
     const int cols = a.cols;
-    const int64_t row = blockIdx.x;
     const int64_t off = row * (int64_t)cols;
     const int stride = rl.W * V;
     const int base = rl.lane * V;
@@ -731,6 +730,11 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
             store_guarded<V, HINT>(Y + off, i0, cols, cols, d);
         }, 0.0f);
     }
+}
+
+template <int OP, int V, int KEEP, int HINT, class T>
+__global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
+    loop_row<OP, V, KEEP, HINT, T>(a, blockIdx.x);
 }
 
 // ---- split rows: several workgroups per row ---------------------------------------

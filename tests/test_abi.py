@@ -328,3 +328,33 @@ def test_split_needs_workspace_and_alignment(L):
         RR_ERR_INVALID_ARGUMENT                                       # workspace not 16-byte aligned
     assert L.rmsnorm_f32_ws(P, P, P, 3, 100003, 1e-6, None, P, -1, None) == RR_ERR_INVALID_ARGUMENT
     assert L.cross_entropy_f32_ws(P, P, P, 3, 100003, p, None, 0, None) == RR_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- batched launch (no launch happens)
+
+def test_batch_argument_errors(L):
+    from row_reduction_amd._capi import RR_BATCH_MAX, rr_problem
+    arr = (rr_problem * (RR_BATCH_MAX + 1))()
+    assert L.rr_batch(arr, -1, None) == RR_ERR_INVALID_ARGUMENT
+    assert L.rr_batch(arr, RR_BATCH_MAX + 1, None) == RR_ERR_INVALID_ARGUMENT
+    assert L.rr_batch(None, 1, None) == RR_ERR_INVALID_ARGUMENT
+    assert L.rr_batch(None, 0, None) == RR_OK        # nothing to do
+    # Zero-row problems are skipped without looking at their pointers.
+    for i in range(3):
+        arr[i].op, arr[i].rows, arr[i].cols = i, 0, 8
+    assert L.rr_batch(arr, 3, None) == RR_OK
+    # One invalid problem fails the whole batch before anything launches.
+    good = rr_problem(op=0, eps=1e-6, rows=4, cols=8, x=0x1000, w=0x2000, y=0x3000)
+    bad_eps = rr_problem(op=0, eps=-1.0, rows=4, cols=8, x=0x1000, w=0x2000, y=0x3000)
+    missing = rr_problem(op=1, rows=4, cols=8, x=0x1000)                 # row sum without `out`
+    unaligned = rr_problem(op=2, rows=4, cols=8, x=0x1002, y=0x3000)     # float x at 2 bytes
+    unknown = rr_problem(op=12, rows=4, cols=8, x=0x1000, y=0x3000)
+    neg_cols = rr_problem(op=2, rows=4, cols=0, x=0x1000, y=0x3000)
+    for bad in (bad_eps, missing, unaligned, unknown, neg_cols):
+        two = (rr_problem * 2)(good, bad)
+        assert L.rr_batch(two, 2, None) == RR_ERR_INVALID_ARGUMENT
+    too_wide = rr_problem(op=2, rows=4, cols=1 << 31, x=0x1000, y=0x3000)
+    assert L.rr_batch((rr_problem * 1)(too_wide), 1, None) == RR_ERR_UNSUPPORTED
+    # More than 2^31 - 1 rows in total: refused, nothing launched.
+    big = rr_problem(op=1, rows=(1 << 30) + 1, cols=1, x=0x1000, row_out=0x2000)
+    assert L.rr_batch((rr_problem * 2)(big, big), 2, None) == RR_ERR_UNSUPPORTED
