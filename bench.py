@@ -321,90 +321,95 @@ def single_call_table(torch, rr, device, reps: int = 200) -> dict:
     res = {"rmsnorm_1x127_native_us": round(e2e(native, reps), 2),
            "rmsnorm_1x127_binding_us": round(e2e(binding, reps), 2)}
 
-    # The operator-coverage set, 24 problems.
-    probs, calls, ccalls = [], [], []
-    keep = []
-    for i, (rows, cols) in enumerate(workloads.FAMILY_SHAPES):
-        d = workloads.family_inputs(rows, cols, 700 + i)
-        t = {k: torch.from_numpy(v).to(device) for k, v in d.items()}
-        keep.append(t)
-        for op in workloads.OPS:
-            kw = {}
-            if op in ("rmsnorm", "layernorm", "residual_layernorm"):
-                kw.update(w=t["gamma"], eps=1e-6 if op == "rmsnorm" else 1e-5)
-            if op in ("layernorm", "residual_layernorm"):
-                kw["beta"] = t["beta"]
-            if op == "residual_layernorm":
-                kw["residual"] = t["residual"]
-            if op == "cross_entropy":
-                kw["targets"] = t["targets"]
-            p, outs = rr.batch_problem(op, t["x"], **kw)
-            probs.append(p)
-            keep.append(outs)
+    def set_latency(shapes, prefix):
+        """The six operators on each shape: separate launches against one batch."""
+        probs, calls, ccalls = [], [], []
+        keep = []
+        for i, (rows, cols) in enumerate(shapes):
+            d = workloads.family_inputs(rows, cols, 700 + i)
+            t = {k: torch.from_numpy(v).to(device) for k, v in d.items()}
+            keep.append(t)
+            for op in workloads.OPS:
+                kw = {}
+                if op in ("rmsnorm", "layernorm", "residual_layernorm"):
+                    kw.update(w=t["gamma"], eps=1e-6 if op == "rmsnorm" else 1e-5)
+                if op in ("layernorm", "residual_layernorm"):
+                    kw["beta"] = t["beta"]
+                if op == "residual_layernorm":
+                    kw["residual"] = t["residual"]
+                if op == "cross_entropy":
+                    kw["targets"] = t["targets"]
+                p, outs = rr.batch_problem(op, t["x"], **kw)
+                probs.append(p)
+                keep.append(outs)
 
-            xp_, op_ = t["x"].data_ptr(), op
-            rows_, cols_ = t["x"].shape
-            if op == "rmsnorm":
-                args = (xp_, t["gamma"].data_ptr(), outs["y"].data_ptr(), rows_, cols_, 1e-6)
-            elif op == "sum":
-                args = (xp_, outs["out"].data_ptr(), rows_, cols_)
-            elif op == "softmax":
-                args = (xp_, outs["y"].data_ptr(), rows_, cols_)
-            elif op == "layernorm":
-                args = (xp_, t["gamma"].data_ptr(), t["beta"].data_ptr(), outs["y"].data_ptr(), rows_, cols_, 1e-5)
-            elif op == "residual_layernorm":
-                args = (xp_, t["residual"].data_ptr(), t["gamma"].data_ptr(), t["beta"].data_ptr(),
-                        outs["y"].data_ptr(), None, rows_, cols_, 1e-5)
-            else:
-                args = (xp_, t["targets"].data_ptr(), outs["out"].data_ptr(), rows_, cols_)
-            ccalls.append((getattr(L, {"sum": "row_sum"}.get(op_, op_) + "_f32"), args))
-
-            def call(op=op, t=t, kw=kw, outs=outs):
+                xp_, op_ = t["x"].data_ptr(), op
+                rows_, cols_ = t["x"].shape
                 if op == "rmsnorm":
-                    rr.rmsnorm_f32(t["x"], kw["w"], kw["eps"], y=outs["y"])
+                    args = (xp_, t["gamma"].data_ptr(), outs["y"].data_ptr(), rows_, cols_, 1e-6)
                 elif op == "sum":
-                    rr.row_sum_f32(t["x"], out=outs["out"])
+                    args = (xp_, outs["out"].data_ptr(), rows_, cols_)
                 elif op == "softmax":
-                    rr.softmax_f32(t["x"], y=outs["y"])
+                    args = (xp_, outs["y"].data_ptr(), rows_, cols_)
                 elif op == "layernorm":
-                    rr.layernorm_f32(t["x"], kw["w"], kw["beta"], kw["eps"], y=outs["y"])
+                    args = (xp_, t["gamma"].data_ptr(), t["beta"].data_ptr(), outs["y"].data_ptr(), rows_, cols_, 1e-5)
                 elif op == "residual_layernorm":
-                    rr.residual_layernorm_f32(t["x"], kw["residual"], kw["w"], kw["beta"], kw["eps"], y=outs["y"])
+                    args = (xp_, t["residual"].data_ptr(), t["gamma"].data_ptr(), t["beta"].data_ptr(),
+                            outs["y"].data_ptr(), None, rows_, cols_, 1e-5)
                 else:
-                    rr.cross_entropy_f32(t["x"], kw["targets"], loss=outs["out"])
-            calls.append(call)
-    arr = (_capi.rr_problem * len(probs))(*probs)
+                    args = (xp_, t["targets"].data_ptr(), outs["out"].data_ptr(), rows_, cols_)
+                ccalls.append((getattr(L, {"sum": "row_sum"}.get(op_, op_) + "_f32"), args))
 
-    def separate():
-        for c in calls:
-            c()
+                def call(op=op, t=t, kw=kw, outs=outs):
+                    if op == "rmsnorm":
+                        rr.rmsnorm_f32(t["x"], kw["w"], kw["eps"], y=outs["y"])
+                    elif op == "sum":
+                        rr.row_sum_f32(t["x"], out=outs["out"])
+                    elif op == "softmax":
+                        rr.softmax_f32(t["x"], y=outs["y"])
+                    elif op == "layernorm":
+                        rr.layernorm_f32(t["x"], kw["w"], kw["beta"], kw["eps"], y=outs["y"])
+                    elif op == "residual_layernorm":
+                        rr.residual_layernorm_f32(t["x"], kw["residual"], kw["w"], kw["beta"], kw["eps"], y=outs["y"])
+                    else:
+                        rr.cross_entropy_f32(t["x"], kw["targets"], loss=outs["out"])
+                calls.append(call)
+        arr = (_capi.rr_problem * len(probs))(*probs)
 
-    def batched():
-        st = L.rr_batch(arr, len(probs), torch.cuda.current_stream().cuda_stream)
-        if st != 0:
-            raise RuntimeError(f"rr_batch failed: {st}")
+        def separate():
+            for c in calls:
+                c()
 
-    def separate_c():
-        for fn, args in ccalls:
-            fn(*args, stream)
-    sep = graph_us(torch, separate, 20)
-    bat = graph_us(torch, batched, 20)
+        def batched():
+            st = L.rr_batch(arr, len(probs), torch.cuda.current_stream().cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"rr_batch failed: {st}")
 
-    def sync(fn):
-        def f():
-            fn()
-            hip.hipStreamSynchronize(stream)
-        return f
-    for _ in range(10):
-        sync(separate)()
-        sync(separate_c)()
-        sync(batched)()
-    res.update({"coverage_set_problems": len(probs),
-                "coverage_set_separate_gpu_us": round(sep["us"], 2),
-                "coverage_set_batched_gpu_us": round(bat["us"], 2),
-                "coverage_set_separate_binding_e2e_us": round(e2e(sync(separate), 50), 2),
-                "coverage_set_separate_c_e2e_us": round(e2e(sync(separate_c), 50), 2),
-                "coverage_set_batched_c_e2e_us": round(e2e(sync(batched), reps), 2)})
+        def separate_c():
+            for fn, args in ccalls:
+                fn(*args, stream)
+        sep = graph_us(torch, separate, 20)
+        bat = graph_us(torch, batched, 20)
+
+        def sync(fn):
+            def f():
+                fn()
+                hip.hipStreamSynchronize(stream)
+            return f
+        for _ in range(10):
+            sync(separate)()
+            sync(separate_c)()
+            sync(batched)()
+        res.update({prefix + "_problems": len(probs),
+                    prefix + "_separate_gpu_us": round(sep["us"], 2),
+                    prefix + "_batched_gpu_us": round(bat["us"], 2),
+                    prefix + "_separate_binding_e2e_us": round(e2e(sync(separate), 50), 2),
+                    prefix + "_separate_c_e2e_us": round(e2e(sync(separate_c), 50), 2),
+                    prefix + "_batched_c_e2e_us": round(e2e(sync(batched), reps), 2)})
+
+    # The pages' operator-coverage set (24 problems), and its tiny part alone.
+    set_latency(workloads.FAMILY_SHAPES, "coverage_set")
+    set_latency(workloads.FAMILY_SHAPES[:2], "tiny_set")
     return res
 
 
