@@ -1031,13 +1031,18 @@ int launch_loop_keep(const Args &a, const Launch &l) {
     return (int)hipGetLastError();
 }
 
-// Streaming plans keep 0 or 32 register slots per lane (the latter for the
-// two-pass operators at V >= 4: 32 / V chunks).
+// Streaming plans keep 0 or 32 register slots per lane (the two-pass
+// operators at V >= 4: 32 / V chunks), or 64 for RMSNorm and softmax, whose
+// instances still fit the 128 registers of a 1024-lane workgroup without
+// spilling (the LayerNorms would spill).
 template <int OP, int V, class T>
 int launch_loop(int slots, const Args &a, const Launch &l) {
     if (slots == 0) return launch_loop_keep<OP, V, 0, T>(a, l);
     if constexpr (V >= 4 && OP != kSum && OP != kCrossEntropy) {
         if (slots == 32) return launch_loop_keep<OP, V, 32 / V, T>(a, l);
+    }
+    if constexpr (V >= 4 && (OP == kRmsNorm || OP == kSoftmax)) {
+        if (slots == 64) return launch_loop_keep<OP, V, 64 / V, T>(a, l);
     }
     return (int)hipErrorInvalidValue;
 }

@@ -211,6 +211,12 @@ def test_streaming_kept_slots_only_for_two_pass_operators(L):
         assert L.rr_check_plan(_capi.OP_IDS[op], 3, 100000, kept) == RR_OK
     for op in ("sum", "cross_entropy"):
         assert L.rr_check_plan(_capi.OP_IDS[op], 3, 100000, kept) == RR_ERR_UNSUPPORTED
+    wide = plan(RR_PATH_LOOP, 1024, 1024, 4, 64)
+    for op in ("rmsnorm", "softmax", "rmsnorm_bf16", "softmax_bf16"):
+        assert L.rr_check_plan(_capi.OP_IDS[op], 3, 100000, wide) == RR_OK
+    for op in ("layernorm", "residual_layernorm", "sum", "cross_entropy"):
+        assert L.rr_check_plan(_capi.OP_IDS[op], 3, 100000, wide) == RR_ERR_UNSUPPORTED
+    assert L.rr_check_plan(0, 3, 100000, plan(RR_PATH_LOOP, 256, 256, 4, 64)) == RR_ERR_UNSUPPORTED
     kept8 = plan(RR_PATH_LOOP, 1024, 1024, 8, 32)
     assert L.rr_check_plan(_capi.OP_IDS["softmax_bf16"], 3, 100000, kept8) == RR_OK
     assert L.rr_check_plan(_capi.OP_IDS["cross_entropy_bf16"], 3, 100000, kept8) == RR_ERR_UNSUPPORTED
@@ -252,7 +258,7 @@ def test_selected_plans_are_legal_and_cover_the_row(L, op, rows, cols):
         assert p.lanes_per_row * p.slots >= cols
     else:
         assert cols > 1024 * 32
-        assert p.slots in (0, 32)
+        assert p.slots in (0, 32, 64)
 
 
 def test_page_packing_arithmetic(L):

@@ -111,7 +111,7 @@ def test_streaming_path_beyond_register_budget(gpu_device, op, cols):
     compare(op, run_gpu(op, d, with_h=True), ref, f"{op} {rows}x{cols} selected")
     for v in (1, 2, 4):
         for block in (256, 1024):
-            for kept in (0, 32):
+            for kept in (0, 32, 64):
                 lp = rr.rr_plan(2, block, block, 1, v, kept)
                 if rr.rr_check_plan(op, rows, cols, lp) != 0:
                     continue
@@ -129,8 +129,10 @@ def test_streaming_kept_slots_on_short_rows(gpu_device, op, cols):
     a = family_host_inputs(op, rows, cols, seed=19)
     ref = run_oracle(op, a)
     d = to_dev(a, gpu_device)
-    for block in (256, 1024):
-        lp = rr.rr_plan(2, block, block, 1, 4, 32)
+    for block, kept in ((256, 32), (1024, 32), (1024, 64)):
+        lp = rr.rr_plan(2, block, block, 1, 4, kept)
+        if rr.rr_check_plan(op, rows, cols, lp) != 0:
+            continue
         what = f"{op} {rows}x{cols} {plans.plan_key(lp)}"
         announce(what)
         compare(op, run_gpu(op, d, plan=lp, with_h=True), ref, what)
