@@ -11,12 +11,15 @@ namespace {
 typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
 
 constexpr int kCopyBlock = 256;
-constexpr int kCopyUnroll = 4;  // float4 packs per thread, issued before any store
+constexpr int kCopyUnroll = 1;  // float4 packs per thread
 
 // Thread t of group g copies packs (g * kCopyUnroll + u) * kCopyBlock + t of
 // n / 4 whole packs; group 0's threads also copy the n % 4 trailing floats.
-// Loads and stores are non-temporal: the fastest plain copy measured on
-// MI355X (6.29 TB/s over 1 GiB moved, against 5.70 TB/s without the hint).
+// One non-temporal 16-byte load and store per thread: the fastest plain copy
+// measured on MI355X (6.63 TB/s over 1 GiB moved; 6.0-6.3 TB/s with 2, 4 or 8
+// packs per thread or 512- and 1024-thread groups, 5.7 TB/s without the
+// non-temporal hints; a 1 GiB read-only stream reaches 7.0 TB/s, a
+// write-only one 6.0 TB/s).
 __global__ void __launch_bounds__(kCopyBlock) copy_kernel(const float *__restrict__ src,
                                                           float *__restrict__ dst, int64_t n) {
     const int64_t packs = n / 4;
