@@ -104,7 +104,7 @@ def run(args) -> int:
     n = 16384 * 8192
     src = torch.zeros(n, dtype=torch.float32, device=device)
     dst = torch.empty_like(src)
-    copy_grid = -(-(n // 4) // (256 * 4)) * 256
+    copy_grid = -(-(n // 4) // 256) * 256   # one float4 per thread, 256-thread groups
     for name, kind, fn, grid, nbytes in (
             ("rr_copy_f32 2^27 floats", "copy", lambda: rr.rr_copy_f32(src, dst), copy_grid, 8 * n),
             ("rr_empty_kernel", "empty", lambda: rr.rr_empty_kernel(), 64, 0)):
