@@ -1,0 +1,179 @@
+"""Memory safety of the kernels' addressing, checked on the host.
+
+A model of the index arithmetic the kernels use (consecutive-worker ownership
+i = (chunk * W + lane) * V + e, the in-bounds window load at
+min(i0, cols - V) whose slots keep only columns >= i0, the guarded store, the
+slice bounds of split rows, the kept chunks of the streaming path) is run
+for every legal plan the library accepts on many shapes. For each it checks
+that every load lies inside the row, that the values a row's reduction uses
+are exactly its columns, each once, and that every column is stored exactly
+once, by the lane that read it. Plans come from the library's own legality
+check (rr_check_plan), so a plan it accepts but this model would refuse
+fails here."""
+import numpy as np
+import pytest
+
+import row_reduction_amd as rr
+from row_reduction_amd import _capi, plans
+from row_reduction_amd._capi import RR_OK, rr_plan
+
+RNG = np.random.default_rng(11)
+COLS = sorted({1, 2, 3, 4, 5, 7, 8, 9, 31, 33, 63, 64, 65, 127, 128, 129, 255, 257, 1000, 1023, 1024, 1025,
+               4095, 4096, 4097, 8191, 8192, 12289, 32767, 32768, 32769, 40000, 65536, 65537}
+              | set(int(c) for c in RNG.integers(1, 70000, 12)))
+
+
+def window(i0, cols, v):
+    """(start, kept-columns mask) of the pack at i0 (numpy arrays over lanes)."""
+    start = np.minimum(i0, cols - v)
+    e = np.arange(v)
+    cols_ = start[:, None] + e[None, :]
+    keep = cols_ >= i0[:, None]
+    return start, cols_, keep
+
+
+def store_cols(i0, cols, end, v):
+    """Columns the guarded store writes for packs at i0 (row end `cols`,
+    slice end `end`): the whole pack when it ends by `end`, else the pack's
+    own window columns before `end`."""
+    start, cols_, keep = window(i0, cols, v)
+    complete = (i0 + v) <= end
+    out = np.where(complete[:, None], i0[:, None] + np.arange(v)[None, :], cols_)
+    mask = np.where(complete[:, None], True, keep & (cols_ < end))
+    return out, mask
+
+
+def check_pass(cols, lanes, v, chunks, first=0, end=None):
+    """Loads, kept values and stores of `chunks` packs per lane of one row
+    (or one slice [first, end)); returns kept and stored column lists."""
+    end = cols if end is None else end
+    lane = np.arange(lanes)
+    kept_all, stored_all = [], []
+    for c in range(chunks):
+        i0 = c * lanes * v + first + lane * v
+        start, cols_, keep = window(i0, cols, v)
+        assert (start >= 0).all() and (start + v <= cols).all(), "load outside the row"
+        use = keep & (cols_ < end)
+        kept_all.append(cols_[use])
+        out, mask = store_cols(i0, cols, end, v)
+        stored = out[mask]
+        assert (stored >= 0).all() and (stored < cols).all(), "store outside the row"
+        # Every stored column was read (and kept) by the same lane in the same pack.
+        assert np.array_equal(np.sort(stored), np.sort(cols_[use])), "store of a column not kept"
+        stored_all.append(stored)
+    return np.concatenate(kept_all), np.concatenate(stored_all)
+
+
+def assert_each_once(values, lo, hi, what):
+    values = np.sort(values)
+    assert np.array_equal(values, np.arange(lo, hi)), what
+
+
+def register_plans(op, rows, cols):
+    out = []
+    for p in plans.candidate_plans(op, rows, cols, include_loop=False):
+        out.append(p)
+    return out
+
+
+@pytest.mark.parametrize("op", ["rmsnorm", "softmax_bf16"])
+def test_register_paths_read_and_write_each_column_once(op):
+    n = 0
+    for cols in COLS:
+        for p in register_plans(op, 5, cols):
+            exact = p.lanes_per_row * p.slots == cols
+            kept, stored = check_pass(cols, p.lanes_per_row, p.v, p.slots // p.v)
+            assert_each_once(kept, 0, cols, f"{op} {cols} {plans.plan_key(p)} kept")
+            assert_each_once(stored, 0, cols, f"{op} {cols} {plans.plan_key(p)} stored")
+            if exact:
+                # Exact instances load without windows: every pack is complete.
+                i0 = np.arange(p.slots // p.v)[:, None] * p.lanes_per_row * p.v + np.arange(p.lanes_per_row) * p.v
+                assert (i0 + p.v <= cols).all()
+            n += 1
+    assert n > 200
+
+
+@pytest.mark.parametrize("op", ["rmsnorm", "softmax", "layernorm_bf16", "sum"])
+def test_streaming_path_with_kept_chunks(op):
+    """Kept chunks (registers) then streamed chunks: every chunk index the
+    kernel touches, including kept chunks past the row's last, is in bounds;
+    the union is each column once."""
+    n = 0
+    for cols in COLS:
+        for block in (64, 256, 1024):
+            for v in (1, 2, 4, 8):
+                for kept_slots in (0, 32, 64):
+                    p = rr_plan(2, block, block, 1, v, kept_slots, 2)
+                    if rr.rr_check_plan(op, 3, cols, p) != RR_OK:
+                        continue
+                    nchunk = -(-cols // (block * v))
+                    keep = kept_slots // v
+                    touched = max(nchunk, keep)          # kept chunks are loaded even past the row
+                    kept, stored = check_pass(cols, block, v, touched)
+                    assert_each_once(kept, 0, cols, f"{op} {cols} {plans.plan_key(p)}")
+                    assert_each_once(stored, 0, cols, f"{op} {cols} {plans.plan_key(p)} stored")
+                    n += 1
+    assert n > 100
+
+
+@pytest.mark.parametrize("op", ["rmsnorm", "softmax_bf16", "layernorm"])
+def test_split_slices_partition_the_row(op):
+    n = 0
+    for cols in [c for c in COLS if c >= 8192] + [100003, 1 << 20, (1 << 20) + 8]:
+        for lanes, slots in ((256, 16), (256, 32), (1024, 32), (64, 16)):
+            v = 8 if op.endswith("_bf16") else 4
+            p = rr_plan(3, lanes, lanes, 1, v, slots, 2)
+            if rr.rr_check_plan(op, 2, cols, p) != RR_OK:
+                continue
+            span = lanes * slots
+            slices = -(-cols // span)
+            kept_all, stored_all = [], []
+            for s in range(slices):
+                first = s * span
+                end = min(first + span, cols)
+                kept, stored = check_pass(cols, lanes, v, slots // v, first, end)
+                assert ((kept >= first) & (kept < end)).all()
+                kept_all.append(kept)
+                stored_all.append(stored)
+            assert_each_once(np.concatenate(kept_all), 0, cols, f"split {op} {cols} {lanes}x{slots}")
+            assert_each_once(np.concatenate(stored_all), 0, cols, f"split {op} {cols} {lanes}x{slots} stored")
+            assert rr.rr_workspace_bytes(op, 2, cols, p) == 2 * slices * 16
+            n += 1
+    assert n > 20
+
+
+def test_packed_groups_never_touch_rows_past_the_end():
+    """Rows of a group past the last row mirror the last row and store
+    nothing: the grid covers every row once."""
+    for rows in (1, 7, 8, 9, 1003):
+        for lanes in (8, 16, 32):
+            for block in (64, 256):
+                R = block // lanes
+                groups = -(-rows // R)
+                row_raw = np.arange(groups)[:, None] * R + np.arange(R)[None, :]
+                row_ok = row_raw < rows
+                row = np.where(row_ok, row_raw, rows - 1)
+                assert (row >= 0).all() and (row < rows).all()
+                assert np.array_equal(np.sort(row_raw[row_ok]), np.arange(rows))
+
+
+def test_batch_blocks_map_to_one_row_of_one_problem():
+    """rr_batch's block -> (problem, row) map: problem i owns blocks
+    [first_block_i, first_block_i + rows_i); zero-row problems own none."""
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        count = int(rng.integers(1, _capi.RR_BATCH_MAX + 1))
+        rows = rng.integers(0, 40, count)
+        nz = rows[rows > 0]
+        if nz.size == 0:
+            continue
+        first = np.concatenate([[0], np.cumsum(nz)[:-1]])
+        seen = []
+        for blk in range(int(nz.sum())):
+            i = 0
+            while i + 1 < nz.size and first[i + 1] <= blk:
+                i += 1
+            r = blk - first[i]
+            assert 0 <= r < nz[i]
+            seen.append((i, r))
+        assert len(set(seen)) == int(nz.sum())
