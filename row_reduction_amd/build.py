@@ -7,11 +7,17 @@ one link step produces ``row_reduction_amd/librowred.so``. Objects go to
 Device code is built with packed-FP32 instruction selection turned off
 (``-target-feature -packed-fp32-ops``); hipcc's host pass warns that it does
 not know that feature, which is expected.
+
+Every kernel instance must keep all its values in registers: the compiler's
+resource report is read for each one, and the build fails if any instance
+needs per-lane scratch memory (a spill). The report's per-instance VGPR,
+scratch, LDS and occupancy figures are written to ``_build/resources.txt``.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -60,15 +66,40 @@ def hip_flags() -> list[str]:
     ]
 
 
-def _run(cmd: list[str]) -> None:
+RESOURCE_KEYS = {"VGPRs": "vgpr", "AGPRs": "agpr", "ScratchSize [bytes/lane]": "scratch",
+                 "Occupancy [waves/SIMD]": "occupancy", "LDS Size [bytes/block]": "lds"}
+
+
+def _resources(lines: list[str]) -> dict:
+    """Per-kernel figures from -Rpass-analysis=kernel-resource-usage remarks."""
+    out, name = {}, None
+    for ln in lines:
+        m = re.search(r"remark: Function Name: (\S+)", ln)
+        if m:
+            name = m.group(1)
+            out[name] = {}
+            continue
+        m = re.search(r"remark:\s+([A-Za-z /\[\]]+?): (\d+)", ln)
+        if m and name and m.group(1) in RESOURCE_KEYS:
+            out[name][RESOURCE_KEYS[m.group(1)]] = int(m.group(2))
+    return out
+
+
+def _run(cmd: list[str]) -> dict:
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    # The host pass's notice about the device-only feature is expected noise.
-    lines = [ln for ln in proc.stdout.splitlines()
-             if "packed-fp32-ops' is not a recognized feature" not in ln]
+    # The host pass's notice about the device-only feature is expected noise;
+    # resource remarks are collected, not printed.
+    raw = proc.stdout.splitlines()
+    res = _resources(raw)
+    lines = [ln for ln in raw
+             if "packed-fp32-ops' is not a recognized feature" not in ln and "kernel-resource-usage" not in ln
+             and not re.match(r"^\s*\d+ \|", ln) and not re.match(r"^\s*\|\s*\^", ln)
+             and not ln.startswith("In file included from")]
     if proc.returncode != 0:
         raise RuntimeError("command failed:\n  " + " ".join(cmd) + "\n" + "\n".join(lines))
     if lines:
         sys.stderr.write("\n".join(lines) + "\n")
+    return res
 
 
 def build(jobs: int | None = None, verbose: bool = False, defines: list[str] | None = None,
@@ -87,17 +118,27 @@ def build(jobs: int | None = None, verbose: bool = False, defines: list[str] | N
     for src in HIP_SOURCES:
         obj = os.path.join(bdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([cc, *hip_flags(), *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
-                     "-o", obj])
+        cmds.append([cc, *hip_flags(), "-Rpass-analysis=kernel-resource-usage",
+                     *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj])
     for src in CXX_SOURCES:
         obj = os.path.join(bdir, src.replace(".cpp", ".o"))
         objs.append(obj)
         cmds.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}",
                      "-I/opt/rocm/include", "-c", os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 4)), 16)
+    resources = {}
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         for fut in [ex.submit(_run, c) for c in cmds]:
-            fut.result()
+            resources.update(fut.result())
+    with open(os.path.join(bdir, "resources.txt"), "w") as fh:
+        for name in sorted(resources):
+            r = resources[name]
+            fh.write(f"{name} vgpr={r.get('vgpr')} agpr={r.get('agpr')} scratch={r.get('scratch')} "
+                     f"lds={r.get('lds')} occupancy={r.get('occupancy')}\n")
+    spilled = sorted(n for n, r in resources.items() if r.get("scratch", 0) > 0)
+    if spilled:
+        raise RuntimeError(f"{len(spilled)} kernel instance(s) use scratch memory (spills): "
+                           + ", ".join(spilled[:5]))
     tmp = lib + f".tmp{os.getpid()}"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, lib)

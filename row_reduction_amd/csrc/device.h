@@ -554,7 +554,7 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
 // rest of the row; the chunks are loaded one after another, every pack in
 // bounds (a pack past the row end reads the row's last window and keeps none
 // of it).
-template <int OP, int V, int KEEP, int HINT, class T>
+template <int OP, int V, int KEEP, int LDSC, int HINT, class T>
 __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
     const T *Wt = static_cast<const T *>(a.w);
     const T *B = static_cast<const T *>(a.beta);
@@ -572,6 +572,10 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
     const T *rr = (OP == kResidualLayerNorm) ? static_cast<const T *>(a.residual) + off : nullptr;
     constexpr int kKeep = KEEP > 0 ? KEEP * V : 1;
     float keep[kKeep];  // chunks 0 .. KEEP-1 of this lane
+    // Chunks KEEP .. KEEP+LDSC-1 of this lane, in LDS (1024-lane groups only;
+    // each lane reads back only the words it wrote, so no barrier is needed).
+    __shared__ float lds_keep[LDSC > 0 ? LDSC * V * 1024 : 1];
+    const int ldsc = LDSC < nchunk - KEEP ? LDSC : (nchunk - KEEP > 0 ? nchunk - KEEP : 0);
 
     // Pack of the row's values (x, or x + residual for residual LayerNorm).
     // The last pass over the row may stream it past the caches (cache policy
@@ -596,7 +600,14 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
         for (int c = 0; c < KEEP; ++c) read_first(c * stride + base, &keep[c * V], fill);
 #pragma unroll
         for (int c = 0; c < KEEP; ++c) visit(c * stride + base, &keep[c * V]);
-        for (int c = KEEP; c < nchunk; ++c) {
+        for (int c = KEEP; c < KEEP + ldsc; ++c) {
+            float d[V];
+            read_first(c * stride + base, d, fill);
+            visit(c * stride + base, d);
+#pragma unroll
+            for (int e = 0; e < V; ++e) lds_keep[((c - KEEP) * V + e) * 1024 + threadIdx.x] = d[e];
+        }
+        for (int c = KEEP + ldsc; c < nchunk; ++c) {
             float d[V];
             read_first(c * stride + base, d, fill);
             visit(c * stride + base, d);
@@ -613,7 +624,13 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
                 emit(c * stride + base, d);
             }
         }
-        for (int c = KEEP; c < nchunk; ++c) {
+        for (int c = KEEP; c < KEEP + ldsc; ++c) {
+            float d[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) d[e] = lds_keep[((c - KEEP) * V + e) * 1024 + threadIdx.x];
+            emit(c * stride + base, d);
+        }
+        for (int c = KEEP + ldsc; c < nchunk; ++c) {
             float d[V];
             read(c * stride + base, d, fill);
             emit(c * stride + base, d);
@@ -732,9 +749,9 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
     }
 }
 
-template <int OP, int V, int KEEP, int HINT, class T>
+template <int OP, int V, int KEEP, int LDSC, int HINT, class T>
 __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
-    loop_row<OP, V, KEEP, HINT, T>(a, blockIdx.x);
+    loop_row<OP, V, KEEP, LDSC, HINT, T>(a, blockIdx.x);
 }
 
 // ---- split rows: several workgroups per row ---------------------------------------
@@ -1020,12 +1037,12 @@ int launch_by_v(int v, int chunks, const Args &a, const Launch &l) {
     }
 }
 
-template <int OP, int V, int KEEP, class T>
+template <int OP, int V, int KEEP, int LDSC, class T>
 int launch_loop_keep(const Args &a, const Launch &l) {
     switch (l.cache) {
-        case 0: hipLaunchKernelGGL((loop_kernel<OP, V, KEEP, hint_of_cache(0), T>), l.grid, l.block, 0, l.stream, a); break;
-        case 1: hipLaunchKernelGGL((loop_kernel<OP, V, KEEP, hint_of_cache(1), T>), l.grid, l.block, 0, l.stream, a); break;
-        case 2: hipLaunchKernelGGL((loop_kernel<OP, V, KEEP, hint_of_cache(2), T>), l.grid, l.block, 0, l.stream, a); break;
+        case 0: hipLaunchKernelGGL((loop_kernel<OP, V, KEEP, LDSC, hint_of_cache(0), T>), l.grid, l.block, 0, l.stream, a); break;
+        case 1: hipLaunchKernelGGL((loop_kernel<OP, V, KEEP, LDSC, hint_of_cache(1), T>), l.grid, l.block, 0, l.stream, a); break;
+        case 2: hipLaunchKernelGGL((loop_kernel<OP, V, KEEP, LDSC, hint_of_cache(2), T>), l.grid, l.block, 0, l.stream, a); break;
         default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();
@@ -1034,15 +1051,24 @@ int launch_loop_keep(const Args &a, const Launch &l) {
 // Streaming plans keep 0 or 32 register slots per lane (the two-pass
 // operators at V >= 4: 32 / V chunks), or 64 for RMSNorm and softmax, whose
 // instances still fit the 128 registers of a 1024-lane workgroup without
-// spilling (the LayerNorms would spill).
+// spilling (the LayerNorms would spill). A 1024-lane plan whose registers are
+// full that way (softmax at 64 slots, the LayerNorms at 32) runs one
+// workgroup per compute unit anyway, so it also keeps the next 32 slots per
+// lane in LDS (128 KiB): a 65536-column float LayerNorm row, or 98304
+// columns of softmax, is then read once. (RMSNorm at 64 slots already holds
+// a 65536-column row; with LDS added its instance would spill.)
 template <int OP, int V, class T>
 int launch_loop(int slots, const Args &a, const Launch &l) {
-    if (slots == 0) return launch_loop_keep<OP, V, 0, T>(a, l);
+    if (slots == 0) return launch_loop_keep<OP, V, 0, 0, T>(a, l);
+    constexpr bool kLn = OP == kLayerNorm || OP == kResidualLayerNorm;
     if constexpr (V >= 4 && OP != kSum && OP != kCrossEntropy) {
-        if (slots == 32) return launch_loop_keep<OP, V, 32 / V, T>(a, l);
+        if (slots == 32) {
+            if (kLn && l.block.x == 1024) return launch_loop_keep<OP, V, 32 / V, (kLn ? 32 / V : 0), T>(a, l);
+            return launch_loop_keep<OP, V, 32 / V, 0, T>(a, l);
+        }
     }
     if constexpr (V >= 4 && (OP == kRmsNorm || OP == kSoftmax)) {
-        if (slots == 64) return launch_loop_keep<OP, V, 64 / V, T>(a, l);
+        if (slots == 64) return launch_loop_keep<OP, V, 64 / V, (OP == kSoftmax ? 32 / V : 0), T>(a, l);
     }
     return (int)hipErrorInvalidValue;
 }

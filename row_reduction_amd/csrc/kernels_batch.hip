@@ -31,8 +31,8 @@ __global__ void __launch_bounds__(64) batch_kernel(const BatchArgs b) {
     const int64_t row = blk - q.first_block;
     switch (q.variant) {
 #define ROWRED_BATCH_CASES(OPID, KOP, WIDE, T)                            \
-    case 2 * (OPID): loop_row<KOP, 1, 0, 0, T>(a, row); break;            \
-    case 2 * (OPID) + 1: loop_row<KOP, WIDE, 0, 0, T>(a, row); break;
+    case 2 * (OPID): loop_row<KOP, 1, 0, 0, 0, T>(a, row); break;            \
+    case 2 * (OPID) + 1: loop_row<KOP, WIDE, 0, 0, 0, T>(a, row); break;
         ROWRED_BATCH_CASES(RR_OP_RMSNORM, kRmsNorm, 4, float)
         ROWRED_BATCH_CASES(RR_OP_SUM, kSum, 4, float)
         ROWRED_BATCH_CASES(RR_OP_SOFTMAX, kSoftmax, 4, float)
