@@ -33,12 +33,13 @@
  *   - Return value is an rr_status. rows == 0 returns RR_OK without touching
  *     the GPU. rows < 0, cols <= 0, a NULL required pointer (when rows > 0), a
  *     pointer not 4-byte aligned, or an eps that is negative or not finite
- *     return RR_ERR_INVALID_ARGUMENT. cols > 2^31-1, a grid beyond the device
+ *     return RR_ERR_INVALID_ARGUMENT. cols > RR_MAX_COLS, a grid beyond the device
  *     limit, or an explicit plan that is illegal for (op, rows, cols) return
  *     RR_ERR_UNSUPPORTED. A launch the HIP runtime refuses returns
  *     RR_ERR_LAUNCH. Nothing is enqueued unless RR_OK is returned.
- *   - No global mutable state: all entry points are reentrant and may be
- *     called concurrently from several host threads.
+ *   - All entry points are reentrant and may be called concurrently from
+ *     several host threads. The only global state is a small cache of the
+ *     plan model's recent choices, guarded by a mutex.
  *   - Arithmetic is float32 (row sum: float64 accumulation, see below); the
  *     order of additions inside a row depends on the plan, as the ownership
  *     map permits.
@@ -94,6 +95,11 @@ typedef enum rr_op {
  *                   per-element operators). Only through the *_ws entry
  *                   points; v = 4 (float) or 8 (bfloat16, cols % 8 == 0),
  *                   slots 16 or 32, cache 2. */
+/* Widest row accepted: 2^31 - 2^20 columns, so that every column index a
+ * kernel forms (a pack start plus up to one chunk or slice span) fits in 32
+ * bits. */
+#define RR_MAX_COLS (((int64_t)1 << 31) - ((int64_t)1 << 20))
+
 typedef enum rr_path {
     RR_PATH_PACKED = 0,
     RR_PATH_ROW = 1,
@@ -323,7 +329,7 @@ int rr_batch(const rr_problem *problems, int32_t count, void *stream);
  * table entry when one exists, else the analytic model's cheapest legal
  * candidate (see rr_model_time_us). Pure host function; no GPU needed.
  * Returns RR_ERR_INVALID_ARGUMENT for an unknown op, rows < 0, cols <= 0 or
- * out == NULL, RR_ERR_UNSUPPORTED for cols > 2^31-1. The selected plan is
+ * out == NULL, RR_ERR_UNSUPPORTED for cols > RR_MAX_COLS. The selected plan is
  * the one the plain entry points launch for suitably aligned pointers (the
  * *_ws forms with a large enough workspace may split few long rows instead). */
 int rr_select_plan(int op, int64_t rows, int64_t cols, rr_plan *out);

@@ -93,6 +93,7 @@ _f32 = ctypes.c_float
 _planp = ctypes.POINTER(rr_plan)
 
 RR_BATCH_MAX = 32
+RR_MAX_COLS = (1 << 31) - (1 << 20)   # widest row (every kernel index fits in 32 bits)
 
 
 class rr_problem(ctypes.Structure):

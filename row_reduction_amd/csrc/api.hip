@@ -23,7 +23,7 @@ bool ok_eps(float eps) { return isfinite(eps) && eps >= 0.0f; }
 
 int check_shape(int64_t rows, int64_t cols) {
     if (rows < 0 || cols <= 0) return RR_ERR_INVALID_ARGUMENT;
-    if (cols > 0x7fffffff) return RR_ERR_UNSUPPORTED;
+    if (cols > RR_MAX_COLS) return RR_ERR_UNSUPPORTED;
     return RR_OK;
 }
 

@@ -177,3 +177,34 @@ def test_batch_blocks_map_to_one_row_of_one_problem():
             assert 0 <= r < nz[i]
             seen.append((i, r))
         assert len(set(seen)) == int(nz.sum())
+
+
+def test_widest_rows_keep_every_index_in_32_bits():
+    """Kernels form column indices in 32-bit ints: for the widest accepted
+    row and every legal streaming plan, the largest index any lane forms
+    (pack starts of every chunk touched, including kept chunks, plus the
+    chunk-count rounding cols + stride - 1) stays below 2^31; one column
+    more is refused."""
+    cols = _capi.RR_MAX_COLS
+    L = _capi.lib()
+    for op in _capi.OP_IDS:
+        assert rr.rr_check_plan(op, 1, cols + 1, rr.rr_select_plan(op, 1, 8)) == _capi.RR_ERR_UNSUPPORTED
+        p = rr.rr_select_plan(op, 1, cols)
+        assert rr.rr_check_plan(op, 1, cols, p) == RR_OK
+        assert L.rr_select_plan(_capi.OP_IDS[op], 1, cols + 1, rr_plan()) == _capi.RR_ERR_UNSUPPORTED
+    n = 0
+    for op in ("rmsnorm", "softmax", "layernorm", "sum_bf16", "softmax_bf16"):
+        for block in (64, 256, 1024):
+            for v in (1, 2, 4, 8):
+                for kept in (0, 32, 64):
+                    p = rr_plan(2, block, block, 1, v, kept, 2)
+                    if rr.rr_check_plan(op, 1, cols, p) != RR_OK:
+                        continue
+                    stride = block * v
+                    nchunk = (cols + stride - 1) // stride
+                    assert cols + stride - 1 < 2 ** 31
+                    last_chunk = max(nchunk, kept // v + 32 // v) - 1   # kept and LDS-kept chunks
+                    biggest = last_chunk * stride + (block - 1) * v + v
+                    assert biggest < 2 ** 31, (op, plans.plan_key(p), biggest)
+                    n += 1
+    assert n > 20
