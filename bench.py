@@ -206,6 +206,13 @@ def shape_table(torch, rr, workloads, device, samples: int = 15) -> list:
     return out
 
 
+def device_info(torch) -> dict:
+    """The GPU the numbers come from (name, ISA, compute units, memory)."""
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count, "memory_GiB": round(p.total_memory / 2 ** 30, 1)}
+
+
 def host_cores() -> int:
     """Host cores available to this process (capped at 16, a one-GPU share)."""
     try:
@@ -563,6 +570,7 @@ def main() -> int:
         "copy_ceiling": {"bytes": 8 * rows * cols, "us": round(copy["us"], 2),
                          "GBps": round(copy_gbps, 1), "frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4)},
         "launch_floor_us": round(empty["us"], 3),
+        "device": device_info(torch),
         "shapes": shapes,
         "long_rows": long_rows,
         "streaming_rows": streaming,
