@@ -410,6 +410,7 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
     constexpr bool kMaxFirst = (OP == kSoftmax || OP == kCrossEntropy);
     __shared__ float lds0[16];
     __shared__ float lds1[16];
+    __shared__ float lds2[16];
     __shared__ double ldsd[16];
 
     const RowLanes<SEG> rl(a);
@@ -504,24 +505,36 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
         }
     } else {
         static_assert(OP == kLayerNorm || OP == kResidualLayerNorm, "unknown operator");
+        // Corrected two-pass statistics: the float32 mean m carries an
+        // absolute error near 2^-24 |m|, which (x - mean) / sqrt(var + eps)
+        // would amplify when the variance is small next to mean^2. The
+        // deviations d = x - m are exact for x near m, so their sum gives
+        // the correction c = sum(d) / n and the outputs use d - c; the
+        // variance is sum(d^2) / n - c^2. Missing columns hold 0.
         float t[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) t[k] = v[k];
-        const float mean = row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds0) / (float)cols;
-        // Deviations; slots past the row end must not count in the variance.
+        const float m = row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds0) / (float)cols;
+        // Deviations; slots past the row end must not count.
 #pragma unroll
         for (int c = 0; c < NCHUNK; ++c) {
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                const float d = v[c * V + e] - mean;
+                const float d = v[c * V + e] - m;
                 const int i0 = c * stride + base;
                 v[c * V + e] = (EXACT || window_start<V>(i0, cols) + e >= i0) ? d : 0.0f;
             }
         }
 #pragma unroll
+        for (int k = 0; k < K; ++k) t[k] = v[k];
+        const float corr = row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds2) / (float)cols;
+#pragma unroll
         for (int k = 0; k < K; ++k) t[k] = v[k] * v[k];
-        const float var = row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds1) / (float)cols;
+        const float q = row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds1) / (float)cols;
+        const float var = fmaxf(q - corr * corr, 0.0f);
         const float rstd = rsqrtf(var + a.eps);
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] -= corr;
         if (row_ok) {
             // All gamma / beta packs are issued before the first store.
             float g[K], b[K];
@@ -541,13 +554,27 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
     }
 }
 
+// The row's first value h0 (x, or x + residual at the tensors' precision),
+// read by every lane: the shift of the LayerNorms' float64 sums.
+template <int OP, class T>
+__device__ __forceinline__ float row_first_value(const Args &a, int64_t off) {
+    float h0;
+    load_pack<1>(static_cast<const T *>(a.x) + off, &h0);
+    if constexpr (OP == kResidualLayerNorm) {
+        float r0;
+        load_pack<1>(static_cast<const T *>(a.residual) + off, &r0);
+        h0 = is_bf16<T> ? round_to_bf16(h0 + r0) : h0 + r0;
+    }
+    return h0;
+}
+
 // ---- streaming kernel for rows beyond the register budget ------------------------
 //
 // One row per workgroup, W = blockDim.x workers, the same ownership map with as
 // many chunks as the row needs. Statistics take a single pass: softmax and
 // cross-entropy keep a running (max, sum of exp) per lane, rescaling the sum
-// when the max grows; LayerNorm keeps a running (count, mean, M2) per lane,
-// merging each pack with Chan's formula; lanes then merge in a fixed order.
+// when the max grows; LayerNorm keeps float64 sums of (h - h0) and
+// (h - h0)^2 with h0 the row's first value; lanes then merge in a fixed order.
 // Passes over the row: RMSNorm 2, softmax 2, LayerNorm 2, cross-entropy 1,
 // row sum 1. The first KEEP chunks of a lane (KEEP * V register slots) stay
 // in registers between the two passes, so the second pass re-reads only the
@@ -562,6 +589,7 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
     __shared__ float lds0[16];
     __shared__ float lds1[16];
     __shared__ double ldsd[16];
+    __shared__ double ldsd2[16];
     const RowLanes<64> rl(a);
     const int cols = a.cols;
     const int64_t off = row * (int64_t)cols;
@@ -710,19 +738,37 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
         }
     } else {
         static_assert(OP == kLayerNorm || OP == kResidualLayerNorm, "unknown operator");
-        float n = 0.0f, mean = 0.0f, m2 = 0.0f;  // running count, mean, sum of squared deviations
+        // Per lane, one pass: a running (count, mean, M2) merged pack by pack
+        // with Chan's formula (the pack deviations and mean differences it
+        // forms are exact for nearby values, so the lane's M2 stays accurate
+        // in float32), and a float64 running sum, so the row mean the outputs
+        // subtract is exact to float64 rounding: a float32 mean would carry
+        // an error near 2^-24 |mean| into every deviation, which
+        // (x - mean) / sqrt(var + eps) amplifies when the variance is small
+        // next to mean^2.
+        // Chan runs on the values shifted by the row's first value h0, so
+        // its running mean stays near the spread of the row rather than its
+        // mean, and rounding the running mean costs nothing measurable.
+        const float h0 = row_first_value<OP, T>(a, off);
+        float n = 0.0f, mean = 0.0f, m2 = 0.0f;
+        double sum = 0.0;
         first_pass([&](int i0, const float *d) {
             const int left = cols - i0;
             const float k = (float)(left >= V ? V : (left > 0 ? left : 0));
             if (k > 0.0f) {
-                float t[V];
+                const int start = window_start<V>(i0, cols);
+                float t[V], u[V];
 #pragma unroll
-                for (int e = 0; e < V; ++e) t[e] = d[e];
+                for (int e = 0; e < V; ++e) {
+                    u[e] = (start + e >= i0) ? d[e] - h0 : 0.0f;
+                    t[e] = u[e];
+                    sum += (start + e >= i0) ? (double)d[e] : 0.0;
+                }
                 const float pm = tree_reduce<V>(t, AddOp{}) / k;
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
-                    const float dv = d[e] - pm;
-                    t[e] = (window_start<V>(i0, cols) + e >= i0) ? dv * dv : 0.0f;
+                    const float dv = u[e] - pm;
+                    t[e] = (start + e >= i0) ? dv * dv : 0.0f;
                 }
                 const float pm2 = tree_reduce<V>(t, AddOp{});
                 const float nn = n + k;
@@ -732,10 +778,13 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
                 n = nn;
             }
         }, 0.0f);
-        const float rmean = row_reduce(n * mean, AddOp{}, rl, lds0) / (float)cols;
-        const float dev = mean - rmean;
-        const float var = row_reduce(m2 + n * dev * dev, AddOp{}, rl, lds1) / (float)cols;
-        const float rstd = rsqrtf(var + a.eps);
+        // Row mean from the float64 sums; the between-lane part of the
+        // variance from each lane's exact mean (its float64 sum over its
+        // count), in float64.
+        const double rmean = row_reduce(sum, AddOp{}, rl, ldsd) / (double)cols;
+        const double dv = n > 0.0f ? sum / (double)n - rmean : 0.0;  // lane mean minus row mean
+        const double var = row_reduce((double)m2 + (double)n * dv * dv, AddOp{}, rl, ldsd2) / (double)cols;
+        const float rstd = (float)(1.0 / sqrt(var + (double)a.eps));
         T *hr = (OP == kResidualLayerNorm && a.h_out != nullptr) ? static_cast<T *>(a.h_out) + off : nullptr;
         second_pass([&](int i0, float *d) {
             float g[V], b[V];
@@ -743,7 +792,7 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
             load_window<V>(Wt, i0, cols, g, 0.0f);
             load_window<V>(B, i0, cols, b, 0.0f);
 #pragma unroll
-            for (int e = 0; e < V; ++e) d[e] = (d[e] - rmean) * rstd * g[e] + b[e];
+            for (int e = 0; e < V; ++e) d[e] = (float)((double)d[e] - rmean) * rstd * g[e] + b[e];
             store_guarded<V, HINT>(Y + off, i0, cols, cols, d);
         }, 0.0f);
     }
@@ -764,8 +813,8 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
 // slice and writes the outputs. Partials:
 //   RMSNorm: (sum x^2, -)          row sum: (sum x, -)
 //   softmax / cross-entropy: (slice max m, sum exp(x - m))
-//   LayerNorm: (slice mean, slice sum of squared deviations), merged with
-//   Chan's pairwise formula so no sum of squares of raw values is formed.
+//   LayerNorm: (sum (h - h0), sum (h - h0)^2) in float64, h0 the row's first
+//   value, which every slice reads; merged by plain sums in slice order.
 
 struct Partial2 {
     double a, b;
@@ -783,6 +832,7 @@ __global__ void __launch_bounds__(1024) split_partial_kernel(const Args a) {
     __shared__ float lds0[16];
     __shared__ float lds1[16];
     __shared__ double ldsd[16];
+    __shared__ double ldsd2[16];
     const RowLanes<64> rl(a);
     const int cols = a.cols;
     const int s = blockIdx.x;
@@ -854,22 +904,20 @@ __global__ void __launch_bounds__(1024) split_partial_kernel(const Args a) {
         out.b = (double)row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds1);
     } else {
         static_assert(OP == kLayerNorm || OP == kResidualLayerNorm, "unknown operator");
-        const float n = (float)(end - first);
-        float t[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) t[k] = v[k];
-        const float mean = row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds0) / n;
+        const double h0 = (double)row_first_value<OP, T>(a, off);
+        double s1 = 0.0, s2 = 0.0;
 #pragma unroll
         for (int c = 0; c < NCHUNK; ++c) {
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                const float d = v[c * V + e] - mean;
                 const int i0 = c * stride + base, j = window_start<V>(i0, cols) + e;
-                t[c * V + e] = (j >= i0 && j < end) ? d * d : 0.0f;
+                const double dd = (j >= i0 && j < end) ? (double)v[c * V + e] - h0 : 0.0;
+                s1 += dd;
+                s2 += dd * dd;
             }
         }
-        out.a = (double)mean;
-        out.b = (double)row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds1);
+        out.a = row_reduce(s1, AddOp{}, rl, ldsd);
+        out.b = row_reduce(s2, AddOp{}, rl, ldsd2);
     }
     if (threadIdx.x == 0) static_cast<Partial2 *>(a.workspace)[row * gridDim.x + s] = out;
 }
@@ -877,7 +925,7 @@ __global__ void __launch_bounds__(1024) split_partial_kernel(const Args a) {
 // Merge of the row's `slices` partials, each lane taking every W-th one in
 // slice order, then the fixed-order row reduction.
 template <int OP>
-__device__ __forceinline__ void merge_partials(const Partial2 *p, int slices, int span, int cols,
+__device__ __forceinline__ void merge_partials(const Partial2 *p, int slices, int cols, double h0,
                                                const RowLanes<64> &rl, double *ldsd0, double *ldsd1,
                                                double &stat0, double &stat1) {
     if constexpr (OP == kRmsNorm || OP == kSum) {
@@ -893,17 +941,16 @@ __device__ __forceinline__ void merge_partials(const Partial2 *p, int slices, in
         stat0 = m;
         stat1 = row_reduce(z, AddOp{}, rl, ldsd1);
     } else {
-        // Chan: mean = sum n_j mean_j / N; M2 = sum (M2_j + n_j (mean_j - mean)^2).
-        double sm = 0.0;
-        for (int j = rl.lane; j < slices; j += rl.W) sm += (double)slice_len(j, span, cols) * p[j].a;
-        const double mean = row_reduce(sm, AddOp{}, rl, ldsd0) / (double)cols;
-        double m2 = 0.0;
+        // Shifted sums: mean = h0 + S1 / n, var = (S2 - S1^2 / n) / n.
+        double a1 = 0.0, a2 = 0.0;
         for (int j = rl.lane; j < slices; j += rl.W) {
-            const double d = p[j].a - mean;
-            m2 += p[j].b + (double)slice_len(j, span, cols) * d * d;
+            a1 += p[j].a;
+            a2 += p[j].b;
         }
-        stat0 = mean;
-        stat1 = row_reduce(m2, AddOp{}, rl, ldsd1) / (double)cols;
+        const double S1 = row_reduce(a1, AddOp{}, rl, ldsd0);
+        const double S2 = row_reduce(a2, AddOp{}, rl, ldsd1);
+        stat0 = h0 + S1 / (double)cols;
+        stat1 = fmax(0.0, (S2 - S1 * (S1 / (double)cols)) / (double)cols);
     }
 }
 
@@ -925,7 +972,9 @@ __global__ void __launch_bounds__(1024) split_final_kernel(const Args a) {
     const int end = first + slice_len(s, span, cols);
     const Partial2 *p = static_cast<const Partial2 *>(a.workspace) + row * slices;
     double stat0 = 0.0, stat1 = 0.0;
-    merge_partials<OP>(p, slices, span, cols, rl, ldsd0, ldsd1, stat0, stat1);
+    double h0 = 0.0;
+    if constexpr (OP == kLayerNorm || OP == kResidualLayerNorm) h0 = (double)row_first_value<OP, T>(a, off);
+    merge_partials<OP>(p, slices, cols, h0, rl, ldsd0, ldsd1, stat0, stat1);
 
     const T *xr = static_cast<const T *>(a.x) + off;
     if constexpr (OP == kSum) {
@@ -950,10 +999,7 @@ __global__ void __launch_bounds__(1024) split_final_kernel(const Args a) {
             shift = (float)stat0;
             scale = (float)(1.0 / stat1);
         }
-        if constexpr (OP == kLayerNorm || OP == kResidualLayerNorm) {
-            shift = (float)stat0;
-            scale = (float)(1.0 / sqrt(stat1 + (double)a.eps));
-        }
+        if constexpr (OP == kLayerNorm || OP == kResidualLayerNorm) scale = (float)(1.0 / sqrt(stat1 + (double)a.eps));
 #pragma unroll
         for (int c = 0; c < NCHUNK; ++c) {
             const int i0 = c * stride + base;
@@ -976,7 +1022,7 @@ __global__ void __launch_bounds__(1024) split_final_kernel(const Args a) {
                 load_window<V>(Wt, i0, cols, w, 0.0f);
                 load_window<V>(B, i0, cols, b, 0.0f);
 #pragma unroll
-                for (int e = 0; e < V; ++e) d[e] = (d[e] - shift) * scale * w[e] + b[e];
+                for (int e = 0; e < V; ++e) d[e] = (float)((double)d[e] - stat0) * scale * w[e] + b[e];
             }
             store_guarded<V, HINT>(Y, i0, cols, end, d);
         }

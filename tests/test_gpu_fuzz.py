@@ -1,0 +1,76 @@
+"""Seeded random shapes for every operator and storage type, run with the
+plan the library selects (table, else the analytic model), with and without
+a split-row workspace, each compared element by element with the CPU
+oracle. The fixed parity matrix names its plans; this covers whatever the
+selector picks across the shape space."""
+import numpy as np
+import pytest
+
+import row_reduction_amd as rr
+from row_reduction_amd import plans, workloads
+
+from parity_util import announce, compare, family_host_inputs, run_oracle, to_dev
+from test_gpu_batch import rename
+from test_gpu_bf16 import compare as compare_bf16
+from test_gpu_bf16 import dev_inputs as dev_inputs_bf16
+from test_gpu_bf16 import run_oracle as run_oracle_bf16
+from test_gpu_split import run_bf16, run_f32
+
+pytestmark = pytest.mark.gpu
+
+OPS = list(workloads.OPS)
+
+
+def shapes(seed, n, max_elems=1 << 22):
+    """n (rows, cols) drawn log-uniformly, at most max_elems elements: every
+    third draw a long row (cols 32768..140000, the streaming and split
+    paths), the others rows 1..20000 and cols 1..140000."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        if len(out) % 3 == 2:
+            cols = int(round(2 ** rng.uniform(15, np.log2(140000))))
+            rows = int(round(2 ** rng.uniform(0, np.log2(max(1, max_elems // cols)))))
+        else:
+            rows = int(round(2 ** rng.uniform(0, np.log2(20000))))
+            cols = int(round(2 ** rng.uniform(0, np.log2(140000))))
+        if rows * cols <= max_elems:
+            out.append((rows, cols))
+    return out
+
+
+@pytest.mark.parametrize("op", OPS)
+def test_selected_plans_on_random_shapes_f32(gpu_device, op):
+    import torch
+    for i, (rows, cols) in enumerate(shapes(8000 + OPS.index(op), 6)):
+        a = family_host_inputs(op, rows, cols, seed=9000 + i)
+        ref = run_oracle(op, a)
+        d = to_dev(a, gpu_device)
+        key = plans.plan_key(rr.rr_select_plan(op, rows, cols))
+        announce(f"fuzz {op} {rows}x{cols} {key}")
+        compare(op, run_f32(op, d, None, None, gpu_device), ref, f"fuzz {op} {rows}x{cols} {key}")
+        nbytes = rr.rr_workspace_bytes(op, rows, cols)
+        if nbytes > 0:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu_device)
+            announce(f"fuzz {op} {rows}x{cols} with workspace")
+            compare(op, run_f32(op, d, None, ws, gpu_device), ref, f"fuzz {op} {rows}x{cols} ws")
+
+
+@pytest.mark.parametrize("op", OPS)
+def test_selected_plans_on_random_shapes_bf16(gpu_device, op):
+    import torch
+    eps = workloads.RMSNORM_EPS if op == "rmsnorm" else workloads.LAYERNORM_EPS
+    for i, (rows, cols) in enumerate(shapes(8100 + OPS.index(op), 6)):
+        if i % 2:
+            cols = max(8, cols - cols % 8)      # half the draws allow 8-wide packs
+        d = workloads.family_inputs_bf16(rows, cols, seed=9100 + i)
+        ref = run_oracle_bf16(op, d, eps)
+        t = dev_inputs_bf16(d, gpu_device)
+        key = plans.plan_key(rr.rr_select_plan(op + "_bf16", rows, cols))
+        announce(f"fuzz {op}_bf16 {rows}x{cols} {key}")
+        compare_bf16(rename(run_bf16(op, t, None, None)), ref, f"fuzz {op}_bf16 {rows}x{cols} {key}")
+        nbytes = rr.rr_workspace_bytes(op + "_bf16", rows, cols)
+        if nbytes > 0:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu_device)
+            announce(f"fuzz {op}_bf16 {rows}x{cols} with workspace")
+            compare_bf16(rename(run_bf16(op, t, None, ws)), ref, f"fuzz {op}_bf16 {rows}x{cols} ws")
