@@ -329,6 +329,17 @@ __device__ __forceinline__ double readlane(double v, int lane) {
     return join(__builtin_amdgcn_readlane(h.lo, lane), __builtin_amdgcn_readlane(h.hi, lane));
 }
 
+// Two float32 sums reduced together: one butterfly step and one LDS slot
+// per wavefront carry both.
+struct F2 {
+    float a, b;
+};
+__device__ __forceinline__ F2 operator+(F2 x, F2 y) { return F2{x.a + y.a, x.b + y.b}; }
+template <int CTRL>
+__device__ __forceinline__ F2 dpp(F2 v) { return F2{dpp<CTRL>(v.a), dpp<CTRL>(v.b)}; }
+__device__ __forceinline__ F2 swizzle_xor16(F2 v) { return F2{swizzle_xor16(v.a), swizzle_xor16(v.b)}; }
+__device__ __forceinline__ F2 readlane(F2 v, int lane) { return F2{readlane(v.a, lane), readlane(v.b, lane)}; }
+
 // Butterfly over aligned segments of SEG lanes (8, 16, 32 or 64). All lanes
 // must be active. Afterwards every lane of a segment holds the same value:
 // each step combines a lane with a partner holding the complementary half
@@ -410,7 +421,7 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
     constexpr bool kMaxFirst = (OP == kSoftmax || OP == kCrossEntropy);
     __shared__ float lds0[16];
     __shared__ float lds1[16];
-    __shared__ float lds2[16];
+    __shared__ F2 lds2[16];
     __shared__ double ldsd[16];
 
     const RowLanes<SEG> rl(a);
@@ -525,12 +536,16 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
                 v[c * V + e] = (EXACT || window_start<V>(i0, cols) + e >= i0) ? d : 0.0f;
             }
         }
+        float t2[K];
 #pragma unroll
-        for (int k = 0; k < K; ++k) t[k] = v[k];
-        const float corr = row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds2) / (float)cols;
-#pragma unroll
-        for (int k = 0; k < K; ++k) t[k] = v[k] * v[k];
-        const float q = row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds1) / (float)cols;
+        for (int k = 0; k < K; ++k) {
+            t[k] = v[k];
+            t2[k] = v[k] * v[k];
+        }
+        // sum(d) and sum(d^2) in one reduction.
+        const F2 cq = row_reduce(F2{tree_reduce<K>(t, AddOp{}), tree_reduce<K>(t2, AddOp{})}, AddOp{}, rl, lds2);
+        const float corr = cq.a / (float)cols;
+        const float q = cq.b / (float)cols;
         const float var = fmaxf(q - corr * corr, 0.0f);
         const float rstd = rsqrtf(var + a.eps);
 #pragma unroll
@@ -752,31 +767,39 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
         const float h0 = row_first_value<OP, T>(a, off);
         float n = 0.0f, mean = 0.0f, m2 = 0.0f;
         double sum = 0.0;
+        // One pack: its values' shifted mean and M2 merged into the lane's
+        // (count, mean, M2), and their float64 sum. FULL: all V columns lie
+        // in the row (every pack but the row's last), so nothing is masked.
+        auto add_pack = [&](auto full, int i0, const float *d, float k) {
+            constexpr bool kFull = decltype(full)::value;
+            const int start = window_start<V>(i0, cols);
+            float t[V], u[V];
+            double s[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const bool in = kFull || start + e >= i0;
+                u[e] = in ? d[e] - h0 : 0.0f;
+                t[e] = u[e];
+                s[e] = in ? (double)d[e] : 0.0;
+            }
+            sum += tree_reduce<V>(s, AddOp{});
+            const float pm = tree_reduce<V>(t, AddOp{}) / k;
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float dv = u[e] - pm;
+                t[e] = (kFull || start + e >= i0) ? dv * dv : 0.0f;
+            }
+            const float pm2 = tree_reduce<V>(t, AddOp{});
+            const float nn = n + k;
+            const float delta = pm - mean;
+            mean += delta * (k / nn);
+            m2 += pm2 + delta * delta * (n * k / nn);
+            n = nn;
+        };
         first_pass([&](int i0, const float *d) {
             const int left = cols - i0;
-            const float k = (float)(left >= V ? V : (left > 0 ? left : 0));
-            if (k > 0.0f) {
-                const int start = window_start<V>(i0, cols);
-                float t[V], u[V];
-#pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    u[e] = (start + e >= i0) ? d[e] - h0 : 0.0f;
-                    t[e] = u[e];
-                    sum += (start + e >= i0) ? (double)d[e] : 0.0;
-                }
-                const float pm = tree_reduce<V>(t, AddOp{}) / k;
-#pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    const float dv = u[e] - pm;
-                    t[e] = (start + e >= i0) ? dv * dv : 0.0f;
-                }
-                const float pm2 = tree_reduce<V>(t, AddOp{});
-                const float nn = n + k;
-                const float delta = pm - mean;
-                mean += delta * (k / nn);
-                m2 += pm2 + delta * delta * (n * k / nn);
-                n = nn;
-            }
+            if (left >= V) add_pack(std::true_type{}, i0, d, (float)V);
+            else if (left > 0) add_pack(std::false_type{}, i0, d, (float)left);
         }, 0.0f);
         // Row mean from the float64 sums; the between-lane part of the
         // variance from each lane's exact mean (its float64 sum over its
