@@ -74,3 +74,32 @@ def test_selected_plans_on_random_shapes_bf16(gpu_device, op):
             ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu_device)
             announce(f"fuzz {op}_bf16 {rows}x{cols} with workspace")
             compare_bf16(rename(run_bf16(op, t, None, ws)), ref, f"fuzz {op}_bf16 {rows}x{cols} ws")
+
+
+@pytest.mark.parametrize("op", OPS)
+def test_random_legal_plans_on_random_shapes(gpu_device, op):
+    """Two random legal plans of the candidate grid (every path, pack width,
+    slot count and cache policy the grid holds) per random shape, float and
+    bfloat16 storage."""
+    eps = workloads.RMSNORM_EPS if op == "rmsnorm" else workloads.LAYERNORM_EPS
+    rng = np.random.default_rng(8200 + OPS.index(op))
+    for i, (rows, cols) in enumerate(shapes(8300 + OPS.index(op), 4, max_elems=1 << 21)):
+        a = family_host_inputs(op, rows, cols, seed=9200 + i)
+        ref = run_oracle(op, a)
+        d = to_dev(a, gpu_device)
+        cands = plans.candidate_plans(op, rows, cols, caches=(0, 1, 2))
+        for j in rng.choice(len(cands), size=min(2, len(cands)), replace=False):
+            p = cands[int(j)]
+            what = f"fuzz-plan {op} {rows}x{cols} {plans.plan_key(p)}"
+            announce(what)
+            compare(op, run_f32(op, d, p, None, gpu_device), ref, what)
+        cols8 = max(8, cols - cols % 8)
+        db = workloads.family_inputs_bf16(rows, cols8, seed=9300 + i)
+        refb = run_oracle_bf16(op, db, eps)
+        t = dev_inputs_bf16(db, gpu_device)
+        cands = plans.candidate_plans(op + "_bf16", rows, cols8, caches=(0, 1, 2))
+        for j in rng.choice(len(cands), size=min(2, len(cands)), replace=False):
+            p = cands[int(j)]
+            what = f"fuzz-plan {op}_bf16 {rows}x{cols8} {plans.plan_key(p)}"
+            announce(what)
+            compare_bf16(rename(run_bf16(op, t, p, None)), refb, what)
