@@ -289,9 +289,10 @@ int cross_entropy_bf16_ws(const uint16_t *logits, const int32_t *targets, float 
  * Many small independent problems in one kernel launch, so that a sequence
  * of tiny operator calls pays one launch instead of one each (the per-launch
  * cost dominates below about 100 KB per call). Meant for small problems:
- * every row takes one 64-lane wavefront on the streaming row body (one pass
- * for statistics, one for outputs), which is slower than the operator's own
- * entry point for large rows. */
+ * rows run the streaming row body (one pass for statistics, one for
+ * outputs) on one 64-lane wavefront each, or on a whole 256-lane workgroup
+ * from 2048 columns up, which is slower than the operator's own entry point
+ * for large problems. */
 
 #define RR_BATCH_MAX 32
 

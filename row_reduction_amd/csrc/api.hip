@@ -454,7 +454,10 @@ int rr_batch(const rr_problem *problems, int32_t count, void *stream) {
         p.cols = a.cols;
         p.variant = 2 * q.op + (wide ? 1 : 0);
         p.eps = a.eps;
-        blocks += a.rows;
+        // A whole group per row from 2048 columns up, else a wavefront per row.
+        p.lanes = a.cols >= 2048 ? 256 : 64;
+        const int64_t per_group = 256 / p.lanes;
+        blocks += (a.rows + per_group - 1) / per_group;
     }
     if (blocks > 0x7fffffff) return RR_ERR_UNSUPPORTED;
     if (n == 0) return RR_OK;

@@ -1,14 +1,16 @@
 // Batched launch: several independent problems of any operators in one
-// kernel. Each 64-thread workgroup takes one row of one problem (the problem
-// whose block range holds blockIdx.x) and runs the streaming row body on it
-// with one wavefront per row: a single pass for the statistics, a second for
-// the outputs where the operator has per-element outputs.
+// kernel. Each 256-thread workgroup serves the problem whose group range
+// holds blockIdx.x, running the streaming row body (a single pass for the
+// statistics, a second for the outputs where the operator has per-element
+// outputs) either on four of its rows, one wavefront each, or on one row with
+// all four wavefronts. Wavefronts past the problem's last row exit: with one
+// wavefront per row the body has no barrier.
 #include "device.h"
 
 namespace rowred {
 namespace {
 
-__global__ void __launch_bounds__(64) batch_kernel(const BatchArgs b) {
+__global__ void __launch_bounds__(256) batch_kernel(const BatchArgs b) {
     const int64_t blk = blockIdx.x;
     int i = 0;
     while (i + 1 < b.count && b.p[i + 1].first_block <= blk) ++i;
@@ -24,11 +26,12 @@ __global__ void __launch_bounds__(64) batch_kernel(const BatchArgs b) {
     a.row_out = q.row_out;
     a.rows = q.rows;
     a.cols = q.cols;
-    a.lanes_per_row = 64;
-    a.log2_lanes = 6;
-    a.rows_per_group = 1;
+    a.lanes_per_row = q.lanes;
+    a.log2_lanes = q.lanes == 256 ? 8 : 6;
+    a.rows_per_group = 256 / q.lanes;
     a.eps = q.eps;
-    const int64_t row = blk - q.first_block;
+    const int64_t row = (blk - q.first_block) * a.rows_per_group + (threadIdx.x >> a.log2_lanes);
+    if (row >= q.rows) return;  // only when lanes == 64: a whole wavefront, no barrier follows
     switch (q.variant) {
 #define ROWRED_BATCH_CASES(OPID, KOP, WIDE, T)                            \
     case 2 * (OPID): loop_row<KOP, 1, 0, 0, 0, T>(a, row); break;            \
@@ -53,7 +56,7 @@ __global__ void __launch_bounds__(64) batch_kernel(const BatchArgs b) {
 }  // namespace
 
 int launch_batch(const BatchArgs &b, int64_t blocks, void *stream) {
-    hipLaunchKernelGGL(batch_kernel, dim3((unsigned)blocks), dim3(64), 0,
+    hipLaunchKernelGGL(batch_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), b);
     return (int)hipGetLastError();
 }

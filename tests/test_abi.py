@@ -361,6 +361,7 @@ def test_batch_argument_errors(L):
         assert L.rr_batch(two, 2, None) == RR_ERR_INVALID_ARGUMENT
     too_wide = rr_problem(op=2, rows=4, cols=1 << 31, x=0x1000, y=0x3000)
     assert L.rr_batch((rr_problem * 1)(too_wide), 1, None) == RR_ERR_UNSUPPORTED
-    # More than 2^31 - 1 rows in total: refused, nothing launched.
-    big = rr_problem(op=1, rows=(1 << 30) + 1, cols=1, x=0x1000, row_out=0x2000)
+    # More than 2^31 - 1 workgroups in total (four short rows per group): refused,
+    # nothing launched.
+    big = rr_problem(op=1, rows=(1 << 32) + 1, cols=1, x=0x1000, row_out=0x2000)
     assert L.rr_batch((rr_problem * 2)(big, big), 2, None) == RR_ERR_UNSUPPORTED

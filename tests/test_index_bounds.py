@@ -157,26 +157,39 @@ def test_packed_groups_never_touch_rows_past_the_end():
                 assert np.array_equal(np.sort(row_raw[row_ok]), np.arange(rows))
 
 
-def test_batch_blocks_map_to_one_row_of_one_problem():
-    """rr_batch's block -> (problem, row) map: problem i owns blocks
-    [first_block_i, first_block_i + rows_i); zero-row problems own none."""
+def test_batch_groups_map_to_rows_of_one_problem():
+    """rr_batch's (group, wavefront) -> (problem, row) map: problem i owns
+    groups [first_i, first_i + ceil(rows_i / R_i)) with R_i = 256 / lanes_i
+    rows per group (lanes 64 below 2048 columns, else 256); each of its rows
+    is served once, and wavefronts past its last row exit (only with one
+    wavefront per row, where no barrier follows)."""
     rng = np.random.default_rng(3)
     for _ in range(200):
         count = int(rng.integers(1, _capi.RR_BATCH_MAX + 1))
         rows = rng.integers(0, 40, count)
-        nz = rows[rows > 0]
-        if nz.size == 0:
+        cols = rng.choice([7, 100, 2047, 2048, 5000], count)
+        keep = rows > 0
+        rows, cols = rows[keep], cols[keep]
+        if rows.size == 0:
             continue
-        first = np.concatenate([[0], np.cumsum(nz)[:-1]])
+        lanes = np.where(cols >= 2048, 256, 64)
+        per_group = 256 // lanes
+        groups = -(-rows // per_group)
+        first = np.concatenate([[0], np.cumsum(groups)[:-1]])
         seen = []
-        for blk in range(int(nz.sum())):
+        for blk in range(int(groups.sum())):
             i = 0
-            while i + 1 < nz.size and first[i + 1] <= blk:
+            while i + 1 < rows.size and first[i + 1] <= blk:
                 i += 1
-            r = blk - first[i]
-            assert 0 <= r < nz[i]
-            seen.append((i, r))
-        assert len(set(seen)) == int(nz.sum())
+            for tid in range(0, 256, 64):          # one wavefront at a time
+                r = (blk - first[i]) * per_group[i] + (tid >> (8 if lanes[i] == 256 else 6))
+                if r >= rows[i]:
+                    assert lanes[i] == 64           # an exiting wavefront never has barrier partners
+                    continue
+                if lanes[i] == 256 and tid > 0:
+                    continue                        # the same row: counted once per group
+                seen.append((i, int(r)))
+        assert len(seen) == len(set(seen)) == int(rows.sum())
 
 
 def test_widest_rows_keep_every_index_in_32_bits():
