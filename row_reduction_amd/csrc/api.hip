@@ -7,6 +7,7 @@
 
 #include <initializer_list>
 
+#include "batch.h"
 #include "internal.h"
 
 namespace rowred {

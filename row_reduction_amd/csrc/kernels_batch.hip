@@ -5,6 +5,7 @@
 // outputs) either on four of its rows, one wavefront each, or on one row with
 // all four wavefronts. Wavefronts past the problem's last row exit: with one
 // wavefront per row the body has no barrier.
+#include "batch.h"
 #include "device.h"
 
 namespace rowred {
