@@ -29,7 +29,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-shapes] [--no-c
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import platform
@@ -51,18 +50,11 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-COUNTED_SOURCES = ("device.h", "internal.h", "kernels_rmsnorm.hip", "plan.cpp", "plan_table.inc")
-
-
 def kernel_source_hash() -> str:
-    """sha256 over the sources that decide which RMSNorm kernel runs and its code."""
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "row_reduction_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name in COUNTED_SOURCES:
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
-    return h.hexdigest()
+    """Fingerprint of the RMSNorm kernel as launched here: its device sources
+    and the selected plan (the counter summary records the same)."""
+    from row_reduction_amd.profile_cases import headline_fingerprint
+    return headline_fingerprint()
 
 
 def counter_traffic(source_hash: str):

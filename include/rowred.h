@@ -241,8 +241,9 @@ int cross_entropy_bf16_ex(const uint16_t *logits, const int32_t *targets, float 
  * of workspace_bytes bytes (16-byte aligned, caller-owned; its contents need
  * no initialisation and are scratch between the two launches of a split
  * plan). With plan == NULL the selector may then pick RR_PATH_SPLIT for
- * shapes with few, long rows when workspace_bytes suffices, else it picks as
- * the plain forms do; an explicit split plan with too small a workspace
+ * shapes with few (under 256), long rows when workspace_bytes suffices and
+ * its measured per-operator cost model predicts the split faster than the
+ * plain plan, else it picks as the plain forms do; an explicit split plan with too small a workspace
  * returns RR_ERR_UNSUPPORTED. Calls that share one workspace on different
  * streams race. rr_workspace_bytes gives the size a plan needs (the selected
  * one when plan == NULL): rows * S * 16 for a split plan, 0 otherwise, or

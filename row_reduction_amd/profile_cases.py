@@ -33,6 +33,29 @@ if ROOT not in sys.path:
 
 PEAK_GBPS = 8000.0
 
+# The device sources the headline RMSNorm kernel instance is compiled from.
+KERNEL_SOURCES = ("device.h", "internal.h", "kernels_rmsnorm.hip")
+
+
+def kernel_fingerprint(plan: dict) -> str:
+    """sha256 of the headline RMSNorm kernel as launched: its device sources
+    and the plan it is launched with (which fixes the instance, the grid and
+    the block). Counter readings stay valid while this is unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(HERE, "csrc")
+    for name in sorted(KERNEL_SOURCES):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    h.update(json.dumps(plan, sort_keys=True).encode())
+    return h.hexdigest()
+
+
+def headline_fingerprint() -> str:
+    """kernel_fingerprint of RMSNorm 16384x8192 with the plan the library selects."""
+    import row_reduction_amd as rr
+    return kernel_fingerprint(rr.rr_select_plan("rmsnorm", 16384, 8192).as_dict())
+
 
 def cases_list(shapes_only=None):
     from row_reduction_amd import workloads
@@ -197,7 +220,6 @@ def counters(args) -> int:
     `bench.py --no-shapes --no-cpu`, which also launches rr_copy_f32 over the
     same 2^27 floats: each counter is scaled by (bytes the copy must move) /
     (what the counter reads for the copy)."""
-    import hashlib
 
     def load(path, counter):
         per = {}
@@ -217,14 +239,6 @@ def counters(args) -> int:
     f_scale, w_scale = 4 * n / f_copy, 4 * n / w_copy
     f_rms, w_rms = avg(fetch[rms_name]) * 1024 * f_scale, avg(write[rms_name]) * 1024 * w_scale
     algorithmic = 8 * n + 4 * 8192
-    # Same scope as bench.py's kernel_source_hash: the sources that decide
-    # which RMSNorm kernel runs and its code.
-    h = hashlib.sha256()
-    csrc = os.path.join(HERE, "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name in ("device.h", "internal.h", "kernels_rmsnorm.hip", "plan.cpp", "plan_table.inc"):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
     print(f"Kernel: `{rms_name}` (rmsnorm_f32 16384x8192, plan from the measured table)")
     print()
     print("| Counter | Copy kernel raw (KiB/dispatch) | Copy bytes known | Scale | RMSNorm raw (KiB/dispatch) | RMSNorm calibrated bytes |")
@@ -235,7 +249,7 @@ def counters(args) -> int:
     print(f"Algorithmic bytes per launch: {algorithmic}; calibrated traffic / algorithmic = "
           f"{(f_rms + w_rms) / algorithmic:.4f}.")
     print()
-    print(f"source_sha256: {h.hexdigest()}")
+    print(f"source_sha256: {headline_fingerprint()}")
     print(f"traffic_bytes_per_launch: {f_rms + w_rms:.0f}")
     return 0
 

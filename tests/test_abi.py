@@ -319,8 +319,9 @@ def test_workspace_bytes(L):
     assert L.rr_workspace_bytes(0, 3, 100003, p) == 3 * 25 * 16
     assert L.rr_workspace_bytes(0, 3, 4096, plan(RR_PATH_ROW, 256, 256, 4, 16)) == 0
     assert L.rr_workspace_bytes(0, 3, 4096, p) == -1                  # illegal plan
-    # Selector with unlimited workspace: few long rows split, many rows do not.
-    assert L.rr_workspace_bytes(0, 3, 100003, None) == 3 * 25 * 16
+    # Selector with unlimited workspace: few long rows split (64-lane slices of
+    # 1024 columns here), many rows and short rows do not.
+    assert L.rr_workspace_bytes(0, 3, 100003, None) == 3 * 98 * 16
     assert L.rr_workspace_bytes(0, 4096, 100003, None) == 0
     assert L.rr_workspace_bytes(0, 3, 4096, None) == 0
     assert L.rr_workspace_bytes(99, 3, 4096, None) == -1

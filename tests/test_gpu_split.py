@@ -26,7 +26,7 @@ def split_plans(op, rows, cols):
     """Explicit split plans legal for the shape."""
     v = 8 if op.endswith("_bf16") else 4
     out = []
-    for lanes, slots in [(64, 16), (256, 16), (256, 32), (1024, 32)]:
+    for lanes, slots in [(64, 16), (128, 16), (256, 16), (512, 16), (256, 32), (1024, 32)]:
         p = rr.rr_plan(RR_PATH_SPLIT, lanes, lanes, 1, v, slots, 2)
         if rr.rr_check_plan(op, rows, cols, p) == 0:
             out.append(p)
@@ -80,9 +80,10 @@ def test_split_f32_matches_oracle(gpu_device, op, shape):
     d = family_host_inputs(op, rows, cols, seed=cols % 997)
     ref = run_oracle(op, d)
     sel = rr.rr_select_plan(op, rows, cols)
+    # With a workspace the selector splits where its cost model predicts the
+    # split faster (the plain plan otherwise); explicit split plans follow.
     nbytes = rr.rr_workspace_bytes(op, rows, cols)
-    assert nbytes > 0, "the selector splits few long rows when given a workspace"
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu_device)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=gpu_device)
     announce(f"split {op} {rows}x{cols} auto (workspace {nbytes} B; plain plan {sel.as_dict()})")
     compare(op, run_f32(op, d, None, ws, gpu_device), ref, f"split {op} {rows}x{cols} auto")
     for p in split_plans(op, rows, cols):
@@ -103,8 +104,7 @@ def test_split_bf16_matches_oracle(gpu_device, op, shape):
     ref = run_oracle_bf16(op, d, eps)
     t = dev_inputs_bf16(d, gpu_device)
     nbytes = rr.rr_workspace_bytes(op + "_bf16", rows, cols)
-    assert nbytes > 0
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu_device)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=gpu_device)
     announce(f"split {op}_bf16 {rows}x{cols} auto")
     compare_bf16(run_bf16(op, t, None, ws), ref, f"split {op}_bf16 {rows}x{cols} auto")
     for p in split_plans(op + "_bf16", rows, cols):
