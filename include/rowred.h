@@ -124,8 +124,12 @@ typedef enum rr_path {
  *   slots           values each worker keeps in registers: chunks * v with
  *                   chunks in {1, 2, 4, 8} and slots <= 32;
  *                   cols <= lanes_per_row * slots. On the LOOP path the
- *                   values kept between the two passes: 0, or 32 for the
- *                   two-pass operators with v >= 4.
+ *                   values kept in registers between the two passes: 0;
+ *                   32 for the two-pass operators with v >= 4; with
+ *                   v >= 4 and 1024-lane groups also 64 (RMSNorm, softmax)
+ *                   and 96 (softmax). 1024-lane softmax plans keeping 64
+ *                   or 96, and LayerNorm plans keeping 32, hold 32 more
+ *                   values per lane in LDS.
  *   cache           cache policy for the row data: 0 = default; 1 = output
  *                   stores non-temporal; 2 = row loads (x, residual) and
  *                   output stores non-temporal (on the LOOP path only the

@@ -636,8 +636,26 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
     };
     auto read_first = [&](int i0, float *d, float fill) { read_pass(std::false_type{}, i0, d, fill); };
     auto read = [&](int i0, float *d, float fill) { read_pass(std::true_type{}, i0, d, fill); };
-    // First pass, chunk c: kept chunks are loaded into `keep` (all of them
-    // issued before any is used), the others into `d`.
+    // Softmax's first pass: the kept chunks are loaded into `keep` and handed
+    // to visit_kept together, then the others are loaded into `d` and
+    // visited one by one.
+    auto first_pass_kept_together = [&](auto visit_kept, auto visit, float fill) {
+#pragma unroll
+        for (int c = 0; c < KEEP; ++c) read_first(c * stride + base, &keep[c * V], fill);
+        visit_kept();
+        for (int c = KEEP; c < KEEP + ldsc; ++c) {
+            float d[V];
+            read_first(c * stride + base, d, fill);
+            visit(c * stride + base, d);
+#pragma unroll
+            for (int e = 0; e < V; ++e) lds_keep[((c - KEEP) * V + e) * 1024 + threadIdx.x] = d[e];
+        }
+        for (int c = KEEP + ldsc; c < nchunk; ++c) {
+            float d[V];
+            read_first(c * stride + base, d, fill);
+            visit(c * stride + base, d);
+        }
+    };
     auto first_pass = [&](auto visit, float fill) {
 #pragma unroll
         for (int c = 0; c < KEEP; ++c) read_first(c * stride + base, &keep[c * V], fill);
@@ -656,7 +674,35 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
             visit(c * stride + base, d);
         }
     };
-    // Second pass: kept chunks come from registers, the others are re-read.
+    // Second pass: kept chunks come from registers (emit_kept), the others
+    // are re-read (emit).
+    auto second_pass_split = [&](auto emit_kept, auto emit, float fill) {
+        // The kept chunks' column offsets are recomputed here from an opaque
+        // copy of `base`, rather than held in registers from the first pass
+        // alongside the kept values.
+        int base2 = base;
+        asm volatile("" : "+v"(base2));
+#pragma unroll
+        for (int c = 0; c < KEEP; ++c) {
+            if (c < nchunk) {
+                float d[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) d[e] = keep[c * V + e];
+                emit_kept(c * stride + base2, d);
+            }
+        }
+        for (int c = KEEP; c < KEEP + ldsc; ++c) {
+            float d[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) d[e] = lds_keep[((c - KEEP) * V + e) * 1024 + threadIdx.x];
+            emit(c * stride + base, d);
+        }
+        for (int c = KEEP + ldsc; c < nchunk; ++c) {
+            float d[V];
+            read(c * stride + base, d, fill);
+            emit(c * stride + base, d);
+        }
+    };
     auto second_pass = [&](auto emit, float fill) {
 #pragma unroll
         for (int c = 0; c < KEEP; ++c) {
@@ -725,8 +771,38 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
                 m = mn;
             }
         };
+        // Softmax keeps exp(x - mk) rather than x in its register chunks, mk
+        // being the lane's max over them, so the second pass scales them by
+        // one factor instead of exponentiating again. They enter the online
+        // (max, sum) first, as one pack: -inf (masked or missing columns)
+        // becomes 0, NaN stays NaN.
+        float mk = -INFINITY;
         if constexpr (OP == kSoftmax) {
-            first_pass(visit, -INFINITY);
+            first_pass_kept_together([&] {
+                if constexpr (KEEP > 0) {
+                    static_assert(kKeep % 4 == 0, "kept slots fold into four accumulators");
+                    float acc[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[j] = keep[j];
+#pragma unroll
+                    for (int i = 4; i < kKeep; ++i) acc[i % 4] = fmaxf(acc[i % 4], keep[i]);
+                    mk = tree_reduce<4>(acc, MaxOp{});
+                    // With mk = -inf every kept value is -inf (exp gives 0)
+                    // or NaN, so any finite reference serves.
+                    const float ref = mk == -INFINITY ? 0.0f : mk;
+#pragma unroll
+                    for (int i = 0; i < kKeep; ++i) keep[i] = exp_nonpos(keep[i] - ref);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[j] = keep[j];
+#pragma unroll
+                    for (int i = 4; i < kKeep; ++i) acc[i % 4] += keep[i];
+                    const float zk = tree_reduce<4>(acc, AddOp{});
+                    const float mn = fmaxf(m, mk);
+                    z = (m == -INFINITY ? 0.0f : z * exp_nonpos(m - mn)) +
+                        (mk == -INFINITY ? 0.0f : zk * exp_nonpos(mk - mn));
+                    m = mn;
+                }
+            }, visit, -INFINITY);
         } else {
             for (int c = 0; c < nchunk; ++c) {
                 float d[V];
@@ -738,7 +814,14 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
         const float zrow = row_reduce(m == -INFINITY ? 0.0f : z * exp_nonpos(m - mrow), AddOp{}, rl, lds1);
         if constexpr (OP == kSoftmax) {
             const float rz = 1.0f / zrow;
-            second_pass([&](int i0, float *d) {
+            // exp(x - mrow) / z for the kept chunks: their exp(x - mk) times
+            // exp(mk - mrow) / z (0 where mk is -inf and the row is not).
+            const float sk = exp_nonpos(mk - mrow) * rz;
+            second_pass_split([&](int i0, float *d) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) d[e] = d[e] * sk;
+                store_guarded<V, HINT>(Y + off, i0, cols, cols, d);
+            }, [&](int i0, float *d) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) d[e] = exp_nonpos(d[e] - mrow) * rz;
                 store_guarded<V, HINT>(Y + off, i0, cols, cols, d);
@@ -921,8 +1004,10 @@ __global__ void __launch_bounds__(1024) split_partial_kernel(const Args a) {
 #pragma unroll
         for (int k = 0; k < K; ++k) t[k] = v[k];
         const float m = row_reduce(tree_reduce<K>(t, MaxOp{}), MaxOp{}, rl, lds0);
+        // A slice of -inf only (masked columns) has max -inf and sum 0.
+        const float ref = m == -INFINITY ? 0.0f : m;
 #pragma unroll
-        for (int k = 0; k < K; ++k) t[k] = exp_nonpos(v[k] - m);
+        for (int k = 0; k < K; ++k) t[k] = exp_nonpos(v[k] - ref);
         out.a = (double)m;
         out.b = (double)row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds1);
     } else {
@@ -959,8 +1044,9 @@ __device__ __forceinline__ void merge_partials(const Partial2 *p, int slices, in
         double m = -INFINITY;
         for (int j = rl.lane; j < slices; j += rl.W) m = fmax(m, p[j].a);
         m = row_reduce(m, MaxOp{}, rl, ldsd0);
-        double z = 0.0;
-        for (int j = rl.lane; j < slices; j += rl.W) z += p[j].b * exp(p[j].a - m);
+        double z = 0.0;  // slices of -inf only add nothing
+        for (int j = rl.lane; j < slices; j += rl.W)
+            if (p[j].a != -INFINITY) z += p[j].b * exp(p[j].a - m);
         stat0 = m;
         stat1 = row_reduce(z, AddOp{}, rl, ldsd1);
     } else {
@@ -1118,14 +1204,15 @@ int launch_loop_keep(const Args &a, const Launch &l) {
 }
 
 // Streaming plans keep 0 or 32 register slots per lane (the two-pass
-// operators at V >= 4: 32 / V chunks), or 64 for RMSNorm and softmax, whose
-// instances still fit the 128 registers of a 1024-lane workgroup without
-// spilling (the LayerNorms would spill). A 1024-lane plan whose registers are
-// full that way (softmax at 64 slots, the LayerNorms at 32) runs one
-// workgroup per compute unit anyway, so it also keeps the next 32 slots per
-// lane in LDS (128 KiB): a 65536-column float LayerNorm row, or 98304
-// columns of softmax, is then read once. (RMSNorm at 64 slots already holds
-// a 65536-column row; with LDS added its instance would spill.)
+// operators at V >= 4: 32 / V chunks), 64 for RMSNorm and softmax, or 96 for
+// softmax, whose instances still fit the 128 registers of a 1024-lane
+// workgroup without spilling (the LayerNorms would spill at 64). A 1024-lane
+// plan whose registers are full that way (softmax at 64 or 96 slots, the
+// LayerNorms at 32) runs one workgroup per compute unit anyway, so it also
+// keeps the next 32 slots per lane in LDS (128 KiB): a 65536-column float
+// LayerNorm row, or 131072 columns of softmax (a 128256-entry vocabulary),
+// is then read once. (RMSNorm at 64 slots already holds a 65536-column row;
+// with LDS added its instance would spill.)
 template <int OP, int V, class T>
 int launch_loop(int slots, const Args &a, const Launch &l) {
     if (slots == 0) return launch_loop_keep<OP, V, 0, 0, T>(a, l);
@@ -1138,6 +1225,9 @@ int launch_loop(int slots, const Args &a, const Launch &l) {
     }
     if constexpr (V >= 4 && (OP == kRmsNorm || OP == kSoftmax)) {
         if (slots == 64) return launch_loop_keep<OP, V, 64 / V, (OP == kSoftmax ? 32 / V : 0), T>(a, l);
+    }
+    if constexpr (V >= 4 && OP == kSoftmax) {
+        if (slots == 96) return launch_loop_keep<OP, V, 96 / V, 32 / V, T>(a, l);
     }
     return (int)hipErrorInvalidValue;
 }

@@ -21,7 +21,7 @@ VS = (1, 2, 4)
 VS_BF16 = (1, 2, 4, 8)
 CHUNKS = (1, 2, 4, 8)
 LOOP_BLOCKS = (256, 1024)
-LOOP_KEPT_SLOTS = (0, 32, 64)   # streaming: register slots kept between the two passes
+LOOP_KEPT_SLOTS = (0, 32, 64, 96)   # streaming: register slots kept between the two passes
 CACHES = (0, 1, 2)
 
 

@@ -220,6 +220,15 @@ def test_streaming_kept_slots_only_for_two_pass_operators(L):
     kept8 = plan(RR_PATH_LOOP, 1024, 1024, 8, 32)
     assert L.rr_check_plan(_capi.OP_IDS["softmax_bf16"], 3, 100000, kept8) == RR_OK
     assert L.rr_check_plan(_capi.OP_IDS["cross_entropy_bf16"], 3, 100000, kept8) == RR_ERR_UNSUPPORTED
+    vocab = plan(RR_PATH_LOOP, 1024, 1024, 4, 96)
+    for op in ("softmax", "softmax_bf16"):
+        assert L.rr_check_plan(_capi.OP_IDS[op], 3, 128256, vocab) == RR_OK
+    for op in ("rmsnorm", "layernorm", "residual_layernorm", "sum", "cross_entropy", "rmsnorm_bf16"):
+        assert L.rr_check_plan(_capi.OP_IDS[op], 3, 128256, vocab) == RR_ERR_UNSUPPORTED
+    assert L.rr_check_plan(_capi.OP_IDS["softmax"], 3, 128256, plan(RR_PATH_LOOP, 256, 256, 4, 96)) == \
+        RR_ERR_UNSUPPORTED
+    assert L.rr_check_plan(_capi.OP_IDS["softmax"], 3, 128256, plan(RR_PATH_LOOP, 1024, 1024, 2, 96)) == \
+        RR_ERR_UNSUPPORTED
 
 
 def test_v_wider_than_row_is_rejected(L):
@@ -258,7 +267,7 @@ def test_selected_plans_are_legal_and_cover_the_row(L, op, rows, cols):
         assert p.lanes_per_row * p.slots >= cols
     else:
         assert cols > 1024 * 32
-        assert p.slots in (0, 32, 64)
+        assert p.slots in (0, 32, 64, 96)
 
 
 def test_page_packing_arithmetic(L):

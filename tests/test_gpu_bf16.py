@@ -201,3 +201,56 @@ def test_bf16_row_sum_integer_rows_exact(gpu_device):
     announce("row_sum_bf16 integers")
     out = rr.row_sum_bf16(to_dev_bf16(x, gpu_device)).cpu().numpy()
     assert np.array_equal(out, xf.astype(np.int64).sum(axis=1).astype(np.float32))
+
+
+@pytest.mark.parametrize("op", ["softmax", "cross_entropy"])
+@pytest.mark.parametrize("cols", [31, 129, 4104, 40000, 70000])
+def test_bf16_masked_entries_every_plan(gpu_device, op, cols):
+    """bfloat16 -inf entries (masked positions) on every legal plan, the
+    streaming plans with kept chunks and the split plans: probability 0 where
+    masked, all mass on a lone survivor, NaN for a fully masked row (as the
+    oracle gives)."""
+    import torch
+    rows = 6
+    d = host_bf16(rows, cols, seed=43 + cols)
+    x = d["x"]
+    neg_inf = np.uint16(0xFF80)
+    rng = np.random.default_rng(cols)
+    x[0, rng.random(cols) < 0.3] = neg_inf
+    x[1, :] = neg_inf
+    x[1, cols // 2] = np.uint16(0x3F00)          # 0.5
+    x[2, :] = neg_inf
+    x[3, : cols // 2] = neg_inf
+    x[4, cols // 2 + 1:] = neg_inf
+    if op == "cross_entropy":
+        t = d["targets"]
+        t[0] = int(np.flatnonzero(x[0] != neg_inf)[0])
+        t[1] = cols // 2
+        t[3] = cols - 1
+        t[4] = 0
+    ref = run_oracle(op, d, eps_of(op))
+    tdev = dev_inputs(d, gpu_device)
+    name = op + "_bf16"
+    cands = plans.candidate_plans(name, rows, cols)
+    for v in (1, 2, 4, 8):
+        for block in (256, 1024):
+            for kept in (0, 32, 64, 96):
+                lp = rr.rr_plan(2, block, block, 1, v, kept)
+                if rr.rr_check_plan(name, rows, cols, lp) == 0:
+                    cands.append(lp)
+    for p in cands:
+        what = f"masked {name} {rows}x{cols} {plans.plan_key(p)}"
+        announce(what)
+        compare(run_gpu(op, tdev, eps_of(op), plan=p), ref, what)
+    for lanes, slots in ((64, 16), (256, 16), (1024, 32)):
+        sp = rr.rr_plan(3, lanes, lanes, 1, 8, slots, 2)
+        if rr.rr_check_plan(name, rows, cols, sp) != 0:
+            continue
+        ws = torch.empty(rr.rr_workspace_bytes(name, rows, cols, sp), dtype=torch.uint8, device=gpu_device)
+        what = f"masked {name} {rows}x{cols} split w{lanes} k{slots}"
+        announce(what)
+        if op == "softmax":
+            got = {"y": rr.softmax_bf16(tdev["x"], plan=sp, workspace=ws)}
+        else:
+            got = {"loss": rr.cross_entropy_bf16(tdev["x"], tdev["targets"], plan=sp, workspace=ws)}
+        compare(got, ref, what)

@@ -111,7 +111,7 @@ def test_streaming_path_beyond_register_budget(gpu_device, op, cols):
     compare(op, run_gpu(op, d, with_h=True), ref, f"{op} {rows}x{cols} selected")
     for v in (1, 2, 4):
         for block in (256, 1024):
-            for kept in (0, 32, 64):
+            for kept in (0, 32, 64, 96):
                 lp = rr.rr_plan(2, block, block, 1, v, kept)
                 if rr.rr_check_plan(op, rows, cols, lp) != 0:
                     continue
@@ -129,7 +129,7 @@ def test_streaming_kept_slots_on_short_rows(gpu_device, op, cols):
     a = family_host_inputs(op, rows, cols, seed=19)
     ref = run_oracle(op, a)
     d = to_dev(a, gpu_device)
-    for block, kept in ((256, 32), (1024, 32), (1024, 64)):
+    for block, kept in ((256, 32), (1024, 32), (1024, 64), (1024, 96)):
         lp = rr.rr_plan(2, block, block, 1, 4, kept)
         if rr.rr_check_plan(op, rows, cols, lp) != 0:
             continue
@@ -251,6 +251,59 @@ def test_cross_entropy_out_of_range_targets_give_nan(gpu_device):
                                     torch.from_numpy(t).to(gpu_device), plan=p).cpu().numpy()
         assert np.isnan(loss[0]) and np.isnan(loss[1]) and np.isnan(loss[4])
         assert_close(loss[[2, 3, 5]], oracle.cross_entropy(d["x"], t)[[2, 3, 5]], "ce valid rows")
+
+
+@pytest.mark.parametrize("op", ["softmax", "cross_entropy"])
+@pytest.mark.parametrize("cols", [31, 129, 4103, 40000, 70001])
+def test_masked_entries_every_plan(gpu_device, op, cols):
+    """-inf entries (masked positions) add exactly 0 to the row's sum of
+    exponentials and get probability 0; a row masked but for one entry puts
+    all its mass there; a fully masked row is NaN throughout, as in the
+    oracle. Every legal plan, the streaming plans with kept register chunks
+    (masked and missing columns inside them) and the split plans."""
+    import torch
+    rows = 6
+    a = family_host_inputs(op, rows, cols, seed=41 + cols)
+    x = a["x"]
+    rng = np.random.default_rng(cols)
+    x[0, rng.random(cols) < 0.3] = -np.inf
+    x[1, :] = -np.inf
+    x[1, cols // 2] = 0.5
+    x[2, :] = -np.inf
+    x[3, : cols // 2] = -np.inf
+    x[4, cols // 2 + 1:] = -np.inf
+    if op == "cross_entropy":
+        t = a["targets"]
+        t[0] = int(np.flatnonzero(np.isfinite(x[0]))[0])
+        t[1] = cols // 2
+        t[3] = cols - 1
+        t[4] = 0
+    ref = run_oracle(op, a)
+    assert np.isnan(ref["y" if op == "softmax" else "loss"][2]).all()
+    d = to_dev(a, gpu_device)
+    cands = plans.candidate_plans(op, rows, cols)
+    for v in (1, 2, 4):
+        for block in (256, 1024):
+            for kept in (0, 32, 64, 96):
+                lp = rr.rr_plan(2, block, block, 1, v, kept)
+                if rr.rr_check_plan(op, rows, cols, lp) == 0:
+                    cands.append(lp)
+    for p in cands:
+        what = f"masked {op} {rows}x{cols} {plans.plan_key(p)}"
+        announce(what)
+        compare(op, run_gpu(op, d, plan=p), ref, what)
+    for lanes, slots in ((64, 16), (256, 16), (1024, 32)):
+        sp = rr.rr_plan(3, lanes, lanes, 1, 4, slots, 2)
+        if rr.rr_check_plan(op, rows, cols, sp) != 0:
+            continue
+        ws = torch.empty(rr.rr_workspace_bytes(op, rows, cols, sp), dtype=torch.uint8, device=gpu_device)
+        what = f"masked {op} {rows}x{cols} split w{lanes} k{slots}"
+        announce(what)
+        if op == "softmax":
+            got = {"y": rr.softmax_f32(d["x"], plan=sp, workspace=ws)}
+        else:
+            got = {"loss": rr.cross_entropy_f32(d["x"], d["targets"], plan=sp, workspace=ws)}
+        compare(op, got, ref, what)
 
 
 def test_cross_entropy_matches_softmax(gpu_device):

@@ -130,6 +130,34 @@ def test_softmax_constant_row_is_uniform(cols):
     assert np.all(y == np.float32(1.0 / cols))
 
 
+@pytest.mark.parametrize("cols", [2, 31, 257, 4103])
+def test_masked_softmax_is_softmax_of_the_survivors(cols):
+    """-inf entries (masked positions): probability exactly 0, and the other
+    entries are the softmax of the unmasked ones alone (scipy on the subset);
+    cross-entropy is the subset's, +inf for a masked target; a fully masked
+    row is NaN."""
+    rng = np.random.default_rng(cols)
+    x = family(3, cols)["x"]
+    mask = rng.random((3, cols)) < 0.4
+    mask[:, 0] = False
+    mask[2, :] = True
+    x[mask] = -np.inf
+    y = oracle.softmax(x)
+    for r in range(2):
+        keep = ~mask[r]
+        assert np.all(y[r, mask[r]] == 0.0)
+        ref = scipy.special.softmax(x[r, keep].astype(np.float64)).astype(np.float32)
+        assert ulp_close(y[r, keep], ref)
+    assert np.isnan(y[2]).all()
+    t = np.array([0, int(np.flatnonzero(mask[1])[0]) if mask[1].any() else 0, 0], np.int32)
+    loss = oracle.cross_entropy(x, t)
+    ref0 = -math.log(scipy.special.softmax(x[0, ~mask[0]].astype(np.float64))[0])
+    assert ulp_close(loss[:1], np.array([ref0], np.float32))
+    if mask[1].any():
+        assert loss[1] == np.inf
+    assert np.isnan(loss[2])
+
+
 @pytest.mark.parametrize("cols", [1, 2, 31, 128, 257, 4103])
 def test_cross_entropy_constant_row_is_log_cols(cols):
     x = np.full((3, cols), 0.5, np.float32)
