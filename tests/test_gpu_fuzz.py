@@ -103,3 +103,41 @@ def test_random_legal_plans_on_random_shapes(gpu_device, op):
             what = f"fuzz-plan {op}_bf16 {rows}x{cols8} {plans.plan_key(p)}"
             announce(what)
             compare_bf16(rename(run_bf16(op, t, p, None)), refb, what)
+
+
+@pytest.mark.parametrize("op", ["softmax", "cross_entropy"])
+def test_masked_rows_on_random_shapes(gpu_device, op):
+    """Random shapes with a random fraction (0 to 95 %) of -inf entries per
+    row, some rows masked in one contiguous run and one row fully masked,
+    with the selected plan and, where the selector splits, with a
+    workspace; cross-entropy targets point at unmasked entries except in
+    the fully masked row."""
+    import torch
+    rng = np.random.default_rng(8400 + (op == "softmax"))
+    for i, (rows, cols) in enumerate(shapes(8500 + (op == "softmax"), 6)):
+        a = family_host_inputs(op, rows, cols, seed=9400 + i)
+        x = a["x"]
+        for r in range(rows):
+            if r % 3 == 1 and cols > 2:
+                lo = int(rng.integers(0, cols - 1))
+                x[r, lo:int(rng.integers(lo + 1, cols))] = -np.inf
+            else:
+                x[r, rng.random(cols) < rng.uniform(0, 0.95)] = -np.inf
+        full = int(rng.integers(0, rows))
+        x[full, :] = -np.inf
+        if op == "cross_entropy":
+            t = a["targets"]
+            for r in range(rows):
+                alive = np.flatnonzero(np.isfinite(x[r]))
+                t[r] = int(rng.choice(alive)) if alive.size else 0
+        ref = run_oracle(op, a)
+        d = to_dev(a, gpu_device)
+        key = plans.plan_key(rr.rr_select_plan(op, rows, cols))
+        what = f"fuzz-masked {op} {rows}x{cols} {key}"
+        announce(what)
+        compare(op, run_f32(op, d, None, None, gpu_device), ref, what)
+        nbytes = rr.rr_workspace_bytes(op, rows, cols)
+        if nbytes > 0:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu_device)
+            announce(what + " with workspace")
+            compare(op, run_f32(op, d, None, ws, gpu_device), ref, what + " ws")
