@@ -588,12 +588,13 @@ __device__ __forceinline__ float row_first_value(const Args &a, int64_t off) {
 // One row per workgroup, W = blockDim.x workers, the same ownership map with as
 // many chunks as the row needs. Statistics take a single pass: softmax and
 // cross-entropy keep a running (max, sum of exp) per lane, rescaling the sum
-// when the max grows; LayerNorm keeps float64 sums of (h - h0) and
-// (h - h0)^2 with h0 the row's first value; lanes then merge in a fixed order.
+// when the max grows; LayerNorm merges each pack's (count, mean, M2) of the
+// values shifted by the row's first value h0 (Chan's formula) and keeps a
+// float64 running sum for the exact mean; lanes then merge in a fixed order.
 // Passes over the row: RMSNorm 2, softmax 2, LayerNorm 2, cross-entropy 1,
 // row sum 1. The first KEEP chunks of a lane (KEEP * V register slots) stay
-// in registers between the two passes, so the second pass re-reads only the
-// rest of the row; the chunks are loaded one after another, every pack in
+// in registers between the two passes, and the next LDSC chunks in LDS, so
+// the second pass re-reads only the rest of the row; every pack is read in
 // bounds (a pack past the row end reads the row's last window and keeps none
 // of it).
 template <int OP, int V, int KEEP, int LDSC, int HINT, class T>
