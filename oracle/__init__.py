@@ -49,6 +49,9 @@ def _load():
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         lib.oracle_rmsnorm_f32.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, ctypes.c_float]
+        lib.oracle_rmsnorm_f32_sampled.argtypes = [_f32p, _f32p, _i64, ctypes.c_float, _i64p, _i64, _f32p]
+        lib.oracle_row_sum_f32_long.argtypes = [_f32p, _i64, _f32p]
+        lib.oracle_softmax_f32_sampled.argtypes = [_f32p, _i64, _i64p, _i64, _f32p]
         lib.oracle_row_sum_f32.argtypes = [_f32p, _f32p, _i64, _i64]
         lib.oracle_softmax_f32.argtypes = [_f32p, _f32p, _i64, _i64]
         lib.oracle_layernorm_f32.argtypes = [_f32p, _f32p, _f32p, _f32p, _i64, _i64, ctypes.c_float]
@@ -118,6 +121,42 @@ def softmax(x):
     rows, cols = x.shape
     y = np.empty_like(x)
     _check(_load().oracle_softmax_f32(_p(x, _f32p), _p(y, _f32p), rows, cols))
+    return y
+
+
+def _row_and_idx(x, idx):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert x.ndim == 1
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    return x, idx
+
+
+def rmsnorm_sampled(x, w, eps, idx):
+    """rmsnorm of the single row x (1-D float32, up to 2^31 columns) at the
+    columns idx only; the row statistic covers the whole row."""
+    x, idx = _row_and_idx(x, idx)
+    w = _f32(w, 1)
+    assert w.shape == x.shape
+    y = np.empty(idx.size, np.float32)
+    _check(_load().oracle_rmsnorm_f32_sampled(_p(x, _f32p), _p(w, _f32p), x.size, eps,
+                                              _p(idx, _i64p), idx.size, _p(y, _f32p)))
+    return y
+
+
+def row_sum_long(x):
+    """sum_c x[c] of the single row x (1-D float32), in float64, no row copy."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(1, np.float32)
+    _check(_load().oracle_row_sum_f32_long(_p(x, _f32p), x.size, _p(out, _f32p)))
+    return out[0]
+
+
+def softmax_sampled(x, idx):
+    """softmax of the single row x (1-D float32) at the columns idx only."""
+    x, idx = _row_and_idx(x, idx)
+    y = np.empty(idx.size, np.float32)
+    _check(_load().oracle_softmax_f32_sampled(_p(x, _f32p), x.size, _p(idx, _i64p), idx.size,
+                                              _p(y, _f32p)))
     return y
 
 

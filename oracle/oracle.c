@@ -281,6 +281,48 @@ int oracle_cross_entropy_bf16(const uint16_t *logits, const int32_t *targets, fl
     return cross_entropy_any(logits, targets, loss, rows, cols, BF16);
 }
 
+/* ---- one very long float32 row, selected outputs ---------------------------
+ * The same definitions as rmsnorm_row, sum_row and softmax_row, evaluated
+ * for a single row read element by element from its float32 storage (no
+ * float64 copy of the row), with outputs only at the n columns idx[] asks
+ * for: rows of up to 2^31 columns then need no row-sized scratch. The row
+ * statistics accumulate in the same order as the full-row versions. */
+
+int oracle_rmsnorm_f32_sampled(const float *x, const float *w, int64_t cols, float eps,
+                               const int64_t *idx, int64_t n, float *y) {
+    if (cols <= 0 || n < 0) return 1;
+    double sum_sq = 0.0;
+    for (int64_t c = 0; c < cols; ++c) sum_sq += (double)x[c] * (double)x[c];
+    double denom = sqrt(sum_sq / (double)cols + (double)eps);
+    for (int64_t k = 0; k < n; ++k) {
+        if (idx[k] < 0 || idx[k] >= cols) return 1;
+        y[k] = (float)((double)x[idx[k]] * (double)w[idx[k]] / denom);
+    }
+    return 0;
+}
+
+int oracle_row_sum_f32_long(const float *x, int64_t cols, float *out) {
+    if (cols <= 0) return 1;
+    double s = 0.0;
+    for (int64_t c = 0; c < cols; ++c) s += (double)x[c];
+    *out = (float)s;
+    return 0;
+}
+
+int oracle_softmax_f32_sampled(const float *x, int64_t cols, const int64_t *idx, int64_t n, float *y) {
+    if (cols <= 0 || n < 0) return 1;
+    double m = (double)x[0];
+    for (int64_t c = 1; c < cols; ++c)
+        if ((double)x[c] > m) m = (double)x[c];
+    double z = 0.0;
+    for (int64_t c = 0; c < cols; ++c) z += exp((double)x[c] - m);
+    for (int64_t k = 0; k < n; ++k) {
+        if (idx[k] < 0 || idx[k] >= cols) return 1;
+        y[k] = (float)(exp((double)x[idx[k]] - m) / z);
+    }
+    return 0;
+}
+
 /* ---- W x V ownership map (consecutive-worker layout) ----------------------
  * W workers cooperate on one row of N elements; each owns runs of V
  * consecutive elements. Element i belongs to worker (i / V) % W, sits in

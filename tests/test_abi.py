@@ -114,6 +114,8 @@ def test_bad_shapes(L, op):
     assert call(L, op, cols=0) == RR_ERR_INVALID_ARGUMENT
     assert call(L, op, cols=-5) == RR_ERR_INVALID_ARGUMENT
     assert call(L, op, cols=1 << 31) == RR_ERR_UNSUPPORTED
+    assert call(L, op, cols=_capi.RR_MAX_COLS + 1) == RR_ERR_UNSUPPORTED
+    assert call(L, op, rows=0, cols=_capi.RR_MAX_COLS) == RR_OK
 
 
 @pytest.mark.parametrize("op", OPS)

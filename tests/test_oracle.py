@@ -424,3 +424,33 @@ def test_bf16_rmsnorm_constant_row_closed_form():
     ref = wf * c / math.sqrt(c * c + float(np.float32(1e-6)))
     ok, exact = _within_bf16_ulp(y[0], ref)
     assert ok and np.array_equal(y[0], y[1])
+
+
+@pytest.mark.parametrize("cols", [1, 2, 31, 257, 4103, 100003])
+def test_sampled_long_row_forms_equal_the_full_row_oracle(cols):
+    """The one-row forms for very long rows (statistic over the whole row,
+    outputs at chosen columns, no float64 copy of the row) give exactly the
+    full-row oracle's values: same definitions, same accumulation order."""
+    rng = np.random.default_rng(cols)
+    x = rng.standard_normal(cols).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, cols).astype(np.float32)
+    idx = np.unique(np.concatenate([[0, cols - 1], rng.integers(0, cols, 64)]))
+    assert np.array_equal(oracle.rmsnorm_sampled(x, w, 1e-6, idx), oracle.rmsnorm(x[None], w, 1e-6)[0][idx])
+    assert np.array_equal(oracle.softmax_sampled(x, idx), oracle.softmax(x[None])[0][idx])
+    assert oracle.row_sum_long(x) == oracle.row_sum(x[None])[0]
+
+
+def test_sampled_long_row_forms_match_numpy_f64():
+    """Against numpy's float64 (pairwise) sums on a 3M-column row: within one
+    float32 ulp of the rounded results."""
+    rng = np.random.default_rng(77)
+    cols = 3_000_017
+    x = rng.standard_normal(cols).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, cols).astype(np.float32)
+    idx = rng.integers(0, cols, 256)
+    x64 = x.astype(np.float64)
+    ref = (x64[idx] * w[idx] / np.sqrt(np.sum(x64 * x64) / cols + np.float64(np.float32(1e-6)))).astype(np.float32)
+    assert ulp_close(oracle.rmsnorm_sampled(x, w, 1e-6, idx), ref)
+    e = np.exp(x64 - x64.max())
+    assert ulp_close(oracle.softmax_sampled(x, idx), (e[idx] / e.sum()).astype(np.float32))
+    assert ulp_close(np.array([oracle.row_sum_long(x)]), np.array([math.fsum(x64)], np.float32))
