@@ -837,37 +837,40 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
         }
     } else {
         static_assert(OP == kLayerNorm || OP == kResidualLayerNorm, "unknown operator");
-        // Per lane, one pass: a running (count, mean, M2) merged pack by pack
+        // Per lane, one pass over u = h - h0, the values shifted by the row's
+        // first value h0: a running (count, mean, M2) merged pack by pack
         // with Chan's formula (the pack deviations and mean differences it
         // forms are exact for nearby values, so the lane's M2 stays accurate
-        // in float32), and a float64 running sum, so the row mean the outputs
-        // subtract is exact to float64 rounding: a float32 mean would carry
-        // an error near 2^-24 |mean| into every deviation, which
-        // (x - mean) / sqrt(var + eps) amplifies when the variance is small
-        // next to mean^2.
-        // Chan runs on the values shifted by the row's first value h0, so
-        // its running mean stays near the spread of the row rather than its
-        // mean, and rounding the running mean costs nothing measurable.
+        // in float32), and a float64 running sum of the packs' float32 sums
+        // of u. The shift is what keeps this accurate when the variance is
+        // small next to mean^2: u is of the order of the row's spread, not of
+        // its mean, so the float32 sums and the running mean round at that
+        // scale, and the row mean h0 + sum(u) / n the outputs subtract is
+        // accurate to it. (An unshifted float32 mean would carry an error
+        // near 2^-24 |mean| into every deviation, which (x - mean) /
+        // sqrt(var + eps) amplifies.) Chan's weights k / (n + k) use the
+        // hardware reciprocal: a 1-ulp error in a weight moves the merged
+        // mean and M2 by far less than their own rounding.
         const float h0 = row_first_value<OP, T>(a, off);
         float n = 0.0f, mean = 0.0f, m2 = 0.0f;
         double sum = 0.0;
         // One pack: its values' shifted mean and M2 merged into the lane's
-        // (count, mean, M2), and their float64 sum. FULL: all V columns lie
-        // in the row (every pack but the row's last), so nothing is masked.
+        // (count, mean, M2), and their shifted sum added to the float64
+        // sum. FULL: all V columns lie in the row (every pack but the row's
+        // last), so nothing is masked.
         auto add_pack = [&](auto full, int i0, const float *d, float k) {
             constexpr bool kFull = decltype(full)::value;
             const int start = window_start<V>(i0, cols);
             float t[V], u[V];
-            double s[V];
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const bool in = kFull || start + e >= i0;
                 u[e] = in ? d[e] - h0 : 0.0f;
                 t[e] = u[e];
-                s[e] = in ? (double)d[e] : 0.0;
             }
-            sum += tree_reduce<V>(s, AddOp{});
-            const float pm = tree_reduce<V>(t, AddOp{}) / k;
+            const float ps = tree_reduce<V>(t, AddOp{});
+            sum += (double)ps;
+            const float pm = ps / k;
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const float dv = u[e] - pm;
@@ -876,8 +879,9 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
             const float pm2 = tree_reduce<V>(t, AddOp{});
             const float nn = n + k;
             const float delta = pm - mean;
-            mean += delta * (k / nn);
-            m2 += pm2 + delta * delta * (n * k / nn);
+            const float wk = k * __builtin_amdgcn_rcpf(nn);
+            mean += delta * wk;
+            m2 += pm2 + delta * delta * (n * wk);
             n = nn;
         };
         first_pass([&](int i0, const float *d) {
@@ -885,13 +889,14 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
             if (left >= V) add_pack(std::true_type{}, i0, d, (float)V);
             else if (left > 0) add_pack(std::false_type{}, i0, d, (float)left);
         }, 0.0f);
-        // Row mean from the float64 sums; the between-lane part of the
-        // variance from each lane's exact mean (its float64 sum over its
-        // count), in float64.
+        // Row mean (minus h0) from the float64 sums; the between-lane part of
+        // the variance from each lane's mean (its float64 sum over its
+        // count), in float64. The outputs take (h - h0) - mean in float32.
         const double rmean = row_reduce(sum, AddOp{}, rl, ldsd) / (double)cols;
         const double dv = n > 0.0f ? sum / (double)n - rmean : 0.0;  // lane mean minus row mean
         const double var = row_reduce((double)m2 + (double)n * dv * dv, AddOp{}, rl, ldsd2) / (double)cols;
         const float rstd = (float)(1.0 / sqrt(var + (double)a.eps));
+        const float mu = (float)rmean;  // row mean minus h0
         T *hr = (OP == kResidualLayerNorm && a.h_out != nullptr) ? static_cast<T *>(a.h_out) + off : nullptr;
         second_pass([&](int i0, float *d) {
             float g[V], b[V];
@@ -899,7 +904,7 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
             load_window<V>(Wt, i0, cols, g, 0.0f);
             load_window<V>(B, i0, cols, b, 0.0f);
 #pragma unroll
-            for (int e = 0; e < V; ++e) d[e] = (float)((double)d[e] - rmean) * rstd * g[e] + b[e];
+            for (int e = 0; e < V; ++e) d[e] = ((d[e] - h0) - mu) * rstd * g[e] + b[e];
             store_guarded<V, HINT>(Y + off, i0, cols, cols, d);
         }, 0.0f);
     }
