@@ -41,13 +41,17 @@ def build(force: bool = True) -> str:
 
 _lib = None
 
+# ORACLE_LIB names another build of oracle.c to load instead (the tests that
+# plant mistakes in a copy of the source and check that the pins catch them).
+_OVERRIDE = os.environ.get("ORACLE_LIB")
+
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if _OVERRIDE is None and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build(force=True)
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(_OVERRIDE or _LIB)
         lib.oracle_rmsnorm_f32.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, ctypes.c_float]
         lib.oracle_rmsnorm_f32_sampled.argtypes = [_f32p, _f32p, _i64, ctypes.c_float, _i64p, _i64, _f32p]
         lib.oracle_row_sum_f32_long.argtypes = [_f32p, _i64, _f32p]

@@ -228,6 +228,18 @@ def test_softmax_rows_sum_to_one(cols):
     assert np.all(np.abs(y.astype(np.float64).sum(axis=1) - 1.0) <= 1e-5)
 
 
+def test_softmax_and_cross_entropy_large_logits_do_not_overflow():
+    """Logits 800 apart: exp of the raw values would overflow even float64;
+    with the row maximum subtracted first the results are exact: the large
+    entry takes all the mass (the other's e^-800 is below float32's range),
+    and the loss is 800 at the small entry, 0 at the large one."""
+    x = np.array([[0.0, 800.0], [800.0, 0.0], [-800.0, 0.0], [0.0, -800.0]], np.float32)
+    y = oracle.softmax(x)
+    assert np.array_equal(y, np.array([[0, 1], [1, 0], [0, 1], [1, 0]], np.float32))
+    loss = oracle.cross_entropy(x, np.array([0, 0, 1, 1], np.int32))
+    assert np.array_equal(loss, np.array([800, 0, 0, 800], np.float32))
+
+
 def test_softmax_shift_invariance_bitwise():
     rng = np.random.default_rng(1)
     x = (rng.integers(-512, 512, size=(4, 129)) / 64.0).astype(np.float32)  # exact in f32
