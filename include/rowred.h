@@ -25,8 +25,8 @@
  *     the caller; all tensors are contiguous row-major float32 (targets int32),
  *     at least 4-byte aligned. Outputs are preallocated by the caller.
  *   - The library allocates nothing, frees nothing and never synchronises: it
- *     enqueues one kernel on `stream` (a hipStream_t; NULL = the default
- *     stream) and returns. Faults during execution surface at the caller's
+ *     enqueues one kernel (two for a split plan) on `stream` (a hipStream_t;
+ *     NULL = the default stream) and returns. Faults during execution surface at the caller's
  *     next synchronisation.
  *   - y may alias x exactly (in-place); any other overlap between an output
  *     and an input is undefined.
@@ -85,7 +85,7 @@ typedef enum rr_op {
  *   RR_PATH_LOOP:   one row per workgroup, any cols: statistics in one pass
  *                   over the row, then (RMSNorm, softmax, LayerNorm,
  *                   residual LayerNorm) a second pass that re-reads the
- *                   values not kept in registers.
+ *                   values not kept in registers or LDS.
  *   RR_PATH_SPLIT:  a row is cut into S = ceil(cols / (lanes_per_row * slots))
  *                   slices, one workgroup each (2 <= S <= 1024, rows <= 65535):
  *                   a first launch keeps each slice in registers and writes
@@ -157,12 +157,17 @@ int rmsnorm_f32(const float *x, const float *w, float *y,
 int row_sum_f32(const float *x, float *out, int64_t rows, int64_t cols, void *stream);
 
 /* Softmax with the row maximum subtracted:
- * y[r,c] = exp(x[r,c] - m_r) / sum_k exp(x[r,k] - m_r), m_r = max_k x[r,k]. */
+ * y[r,c] = exp(x[r,c] - m_r) / sum_k exp(x[r,k] - m_r), m_r = max_k x[r,k].
+ * -inf entries (masked positions) get 0; a row of -inf only gives NaN, as
+ * the definition does (-inf - -inf). */
 int softmax_f32(const float *x, float *y, int64_t rows, int64_t cols, void *stream);
 
 /* LayerNorm: y = (x - mean_r) / sqrt(var_r + eps) * gamma[c] + beta[c], with
- * the population variance var_r = mean_c (x[r,c] - mean_r)^2 (two passes over
- * the register-resident row). gamma, beta: cols floats. */
+ * the population variance var_r = mean_c (x[r,c] - mean_r)^2. Rows held in
+ * registers take corrected two-pass statistics; longer rows take one pass
+ * that merges per-pack statistics of the values shifted by the row's first
+ * value, so rows whose variance is tiny next to mean^2 stay accurate either
+ * way. gamma, beta: cols floats. */
 int layernorm_f32(const float *x, const float *gamma, const float *beta, float *y,
                   int64_t rows, int64_t cols, float eps, void *stream);
 
@@ -176,6 +181,7 @@ int residual_layernorm_f32(const float *x, const float *residual,
 
 /* Cross-entropy per row with int32 class targets:
  * loss[r] = log sum_c exp(x[r,c] - m_r) + m_r - x[r, targets[r]].
+ * -inf logits add nothing to the sum; a -inf target logit gives +inf.
  * Targets are not validated on the host (that would need a synchronisation):
  * a target outside [0, cols) yields loss = NaN and no out-of-bounds read.
  * targets, loss: rows elements. */
