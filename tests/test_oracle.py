@@ -466,3 +466,23 @@ def test_sampled_long_row_forms_match_numpy_f64():
     e = np.exp(x64 - x64.max())
     assert ulp_close(oracle.softmax_sampled(x, idx), (e[idx] / e.sum()).astype(np.float32))
     assert ulp_close(np.array([oracle.row_sum_long(x)]), np.array([math.fsum(x64)], np.float32))
+
+
+@pytest.mark.parametrize("cols", [1, 2, 3, 31, 33, 127, 128, 129, 257])
+def test_every_operator_matches_pure_python_brute_force(cols):
+    """Every operator against tests/brute.py (pure Python: math.fsum sums,
+    float64 sqrt/exp/log, one rounding) on tiny inputs, within one float32
+    ulp."""
+    import brute
+    d = family(5, cols, seed=cols)
+    x, g, b, r, t = d["x"], d["gamma"], d["beta"], d["residual"], d["targets"]
+    w = g
+    assert ulp_close(oracle.rmsnorm(x, w, 1e-6), brute.rmsnorm(x, w, 1e-6))
+    assert ulp_close(oracle.row_sum(x), brute.row_sum(x))
+    assert ulp_close(oracle.softmax(x), brute.softmax(x))
+    assert ulp_close(oracle.layernorm(x, g, b, 1e-5), brute.layernorm(x, g, b, 1e-5))
+    y, h = oracle.residual_layernorm(x, r, g, b, 1e-5)
+    yb, hb = brute.residual_layernorm(x, r, g, b, 1e-5)
+    assert np.array_equal(h, hb)
+    assert ulp_close(y, yb)
+    assert ulp_close(oracle.cross_entropy(x, t), brute.cross_entropy(x, t))
