@@ -455,7 +455,9 @@ def cpu_baseline(workloads, x_np, w_np, eps, y_gpu_sample, budget_s: float = 10.
         pass
     return {"value": round(gbps(dn, tn), 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "us_per_op_full_shape": round(tn / dn * rows * 1e6, 1),
+            "rows_per_s": round(dn / tn, 1),
             "single_thread_GBps": round(gbps(d1, t1), 3),
+            "single_thread_rows_per_s": round(d1 / t1, 1),
             "sample": f"rmsnorm_f32 16384x8192 input in blocks of {block} rows: {dn} rows on "
                       f"{cores} threads in {tn:.1f} s, {d1} rows on 1 thread in {t1:.1f} s "
                       "(fp64 C loops, static row split)",
@@ -571,6 +573,7 @@ def main() -> int:
     if not args.no_cpu:
         log(f"cpu baseline ({args.cpu_seconds:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(workloads, wl.x, wl.w, wl.eps, y_sample, args.cpu_seconds)
+        result["cpu_baseline"]["gpu_over_oracle"] = round(value / result["cpu_baseline"]["value"], 1)
     else:
         result["cpu_baseline"] = None
     _ = np
