@@ -637,6 +637,36 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
     };
     auto read_first = [&](int i0, float *d, float fill) { read_pass(std::false_type{}, i0, d, fill); };
     auto read = [&](int i0, float *d, float fill) { read_pass(std::true_type{}, i0, d, fill); };
+    // First pass over the LDS-kept chunks: each is loaded, visited and
+    // written to LDS. With one 1024-lane group per compute unit, one load in
+    // flight per lane would leave the memory system idle between chunks, so
+    // kLdsBatch chunks are loaded together where the registers allow it
+    // (4 for LayerNorm's 32 kept slots, 2 for residual LayerNorm and for 64
+    // slots, 1 beside the 96-slot softmax plan).
+    constexpr int kLdsBatch = (KEEP * V <= 32 && OP != kResidualLayerNorm) ? 4 : (KEEP * V <= 64 ? 2 : 1);
+    auto lds_chunks = [&](auto visit, float fill) {
+        int c = KEEP;
+        if constexpr (LDSC > 0 && kLdsBatch > 1) {
+            for (; c + kLdsBatch <= KEEP + ldsc; c += kLdsBatch) {
+                float d[kLdsBatch][V];
+#pragma unroll
+                for (int j = 0; j < kLdsBatch; ++j) read_first((c + j) * stride + base, d[j], fill);
+#pragma unroll
+                for (int j = 0; j < kLdsBatch; ++j) {
+                    visit((c + j) * stride + base, d[j]);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) lds_keep[((c + j - KEEP) * V + e) * 1024 + threadIdx.x] = d[j][e];
+                }
+            }
+        }
+        for (; c < KEEP + ldsc; ++c) {
+            float d[V];
+            read_first(c * stride + base, d, fill);
+            visit(c * stride + base, d);
+#pragma unroll
+            for (int e = 0; e < V; ++e) lds_keep[((c - KEEP) * V + e) * 1024 + threadIdx.x] = d[e];
+        }
+    };
     // Softmax's first pass: the kept chunks are loaded into `keep` and handed
     // to visit_kept together, then the others are loaded into `d` and
     // visited one by one.
@@ -644,13 +674,7 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
 #pragma unroll
         for (int c = 0; c < KEEP; ++c) read_first(c * stride + base, &keep[c * V], fill);
         visit_kept();
-        for (int c = KEEP; c < KEEP + ldsc; ++c) {
-            float d[V];
-            read_first(c * stride + base, d, fill);
-            visit(c * stride + base, d);
-#pragma unroll
-            for (int e = 0; e < V; ++e) lds_keep[((c - KEEP) * V + e) * 1024 + threadIdx.x] = d[e];
-        }
+        lds_chunks(visit, fill);
         for (int c = KEEP + ldsc; c < nchunk; ++c) {
             float d[V];
             read_first(c * stride + base, d, fill);
@@ -662,13 +686,7 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
         for (int c = 0; c < KEEP; ++c) read_first(c * stride + base, &keep[c * V], fill);
 #pragma unroll
         for (int c = 0; c < KEEP; ++c) visit(c * stride + base, &keep[c * V]);
-        for (int c = KEEP; c < KEEP + ldsc; ++c) {
-            float d[V];
-            read_first(c * stride + base, d, fill);
-            visit(c * stride + base, d);
-#pragma unroll
-            for (int e = 0; e < V; ++e) lds_keep[((c - KEEP) * V + e) * 1024 + threadIdx.x] = d[e];
-        }
+        lds_chunks(visit, fill);
         for (int c = KEEP + ldsc; c < nchunk; ++c) {
             float d[V];
             read_first(c * stride + base, d, fill);
