@@ -644,6 +644,45 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
     // (4 for LayerNorm's 32 kept slots, 2 for residual LayerNorm and for 64
     // slots, 1 beside the 96-slot softmax plan).
     constexpr int kLdsBatch = (KEEP * V <= 32 && OP != kResidualLayerNorm) ? 4 : (KEEP * V <= 64 ? 2 : 1);
+    // The chunks beyond the kept ones, streamed in the first pass and re-read
+    // in the second: with the group alone on its compute unit (LDS in use),
+    // kLdsBatch (first pass) or 2 (second pass) loads are kept in flight.
+    constexpr int kStreamBatch1 = LDSC > 0 ? kLdsBatch : 1;
+    constexpr int kStreamBatch2 = (LDSC > 0 && kLdsBatch > 1) ? 2 : 1;
+    auto stream_first = [&](auto visit, float fill) {
+        int c = KEEP + ldsc;
+        if constexpr (kStreamBatch1 > 1) {
+            for (; c + kStreamBatch1 <= nchunk; c += kStreamBatch1) {
+                float d[kStreamBatch1][V];
+#pragma unroll
+                for (int j = 0; j < kStreamBatch1; ++j) read_first((c + j) * stride + base, d[j], fill);
+#pragma unroll
+                for (int j = 0; j < kStreamBatch1; ++j) visit((c + j) * stride + base, d[j]);
+            }
+        }
+        for (; c < nchunk; ++c) {
+            float d[V];
+            read_first(c * stride + base, d, fill);
+            visit(c * stride + base, d);
+        }
+    };
+    auto stream_second = [&](auto emit, float fill) {
+        int c = KEEP + ldsc;
+        if constexpr (kStreamBatch2 > 1) {
+            for (; c + kStreamBatch2 <= nchunk; c += kStreamBatch2) {
+                float d[kStreamBatch2][V];
+#pragma unroll
+                for (int j = 0; j < kStreamBatch2; ++j) read((c + j) * stride + base, d[j], fill);
+#pragma unroll
+                for (int j = 0; j < kStreamBatch2; ++j) emit((c + j) * stride + base, d[j]);
+            }
+        }
+        for (; c < nchunk; ++c) {
+            float d[V];
+            read(c * stride + base, d, fill);
+            emit(c * stride + base, d);
+        }
+    };
     auto lds_chunks = [&](auto visit, float fill) {
         int c = KEEP;
         if constexpr (LDSC > 0 && kLdsBatch > 1) {
@@ -675,11 +714,7 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
         for (int c = 0; c < KEEP; ++c) read_first(c * stride + base, &keep[c * V], fill);
         visit_kept();
         lds_chunks(visit, fill);
-        for (int c = KEEP + ldsc; c < nchunk; ++c) {
-            float d[V];
-            read_first(c * stride + base, d, fill);
-            visit(c * stride + base, d);
-        }
+        stream_first(visit, fill);
     };
     auto first_pass = [&](auto visit, float fill) {
 #pragma unroll
@@ -687,11 +722,7 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
 #pragma unroll
         for (int c = 0; c < KEEP; ++c) visit(c * stride + base, &keep[c * V]);
         lds_chunks(visit, fill);
-        for (int c = KEEP + ldsc; c < nchunk; ++c) {
-            float d[V];
-            read_first(c * stride + base, d, fill);
-            visit(c * stride + base, d);
-        }
+        stream_first(visit, fill);
     };
     // Second pass: kept chunks come from registers (emit_kept), the others
     // are re-read (emit).
@@ -716,11 +747,7 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
             for (int e = 0; e < V; ++e) d[e] = lds_keep[((c - KEEP) * V + e) * 1024 + threadIdx.x];
             emit(c * stride + base, d);
         }
-        for (int c = KEEP + ldsc; c < nchunk; ++c) {
-            float d[V];
-            read(c * stride + base, d, fill);
-            emit(c * stride + base, d);
-        }
+        stream_second(emit, fill);
     };
     auto second_pass = [&](auto emit, float fill) {
 #pragma unroll
@@ -738,11 +765,7 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
             for (int e = 0; e < V; ++e) d[e] = lds_keep[((c - KEEP) * V + e) * 1024 + threadIdx.x];
             emit(c * stride + base, d);
         }
-        for (int c = KEEP + ldsc; c < nchunk; ++c) {
-            float d[V];
-            read(c * stride + base, d, fill);
-            emit(c * stride + base, d);
-        }
+        stream_second(emit, fill);
     };
 
     if constexpr (OP == kRmsNorm) {
