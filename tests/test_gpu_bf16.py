@@ -254,3 +254,27 @@ def test_bf16_masked_entries_every_plan(gpu_device, op, cols):
         else:
             got = {"loss": rr.cross_entropy_bf16(tdev["x"], tdev["targets"], plan=sp, workspace=ws)}
         compare(got, ref, what)
+
+
+@pytest.mark.parametrize("op,slots,cols", [
+    ("layernorm", 32, 32776), ("layernorm", 32, 49152), ("layernorm", 32, 65536), ("layernorm", 32, 98312),
+    ("softmax", 64, 65544), ("softmax", 64, 90000), ("softmax", 64, 131072)])
+def test_bf16_lds_kept_chunks(gpu_device, op, slots, cols):
+    """1024-lane streaming plans whose chunks past the register-kept ones go
+    to LDS (for 16-byte bfloat16 packs straight from memory): the first
+    LDS chunk partly filled, LDS full, and chunks streamed past it; one row
+    offset by a large mean (LayerNorm statistics of shifted values), one
+    ramp, the rest the standard recipe."""
+    rows = 4
+    d = host_bf16(rows, cols, seed=500 + cols)
+    xf = oracle.bf16_to_float(d["x"]).astype(np.float32)
+    xf[1] = xf[1] * 0.01 + 300.0
+    xf[2] = np.linspace(-8.0, 8.0, cols, dtype=np.float32)
+    d["x"] = workloads.as_bf16_bits(xf)
+    ref = run_oracle(op, d, eps_of(op))
+    t = dev_inputs(d, gpu_device)
+    p = rr.rr_plan(2, 1024, 1024, 1, 8, slots, 2)
+    assert rr.rr_check_plan(op + "_bf16", rows, cols, p) == 0
+    what = f"lds-kept {op}_bf16 {rows}x{cols} k{slots}"
+    announce(what)
+    compare(run_gpu(op, t, eps_of(op), plan=p), ref, what)
