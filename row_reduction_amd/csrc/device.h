@@ -913,7 +913,31 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
                 }
             }, visit, -INFINITY);
         } else {
-            for (int c = 0; c < nchunk; ++c) {
+            // Two packs per (max, sum) update: one rescaling exponential and
+            // one max merge per 2V values instead of per V (cross-entropy
+            // 2048x128256 -1 %, bf16 -1.5 to -5 %; four or eight packs measured
+            // the same or slower).
+            constexpr int U = 2;
+            auto visit_u = [&](const float *d) {
+                float t[U * V];
+#pragma unroll
+                for (int e = 0; e < U * V; ++e) t[e] = d[e];
+                const float mn = fmaxf(m, tree_reduce<U * V>(t, MaxOp{}));
+                if (mn != -INFINITY) {
+#pragma unroll
+                    for (int e = 0; e < U * V; ++e) t[e] = exp_nonpos(d[e] - mn);
+                    z = z * exp_nonpos(m - mn) + tree_reduce<U * V>(t, AddOp{});
+                    m = mn;
+                }
+            };
+            int c = 0;
+            for (; c + U <= nchunk; c += U) {
+                float d[U * V];
+#pragma unroll
+                for (int u = 0; u < U; ++u) read((c + u) * stride + base, d + u * V, -INFINITY);
+                visit_u(d);
+            }
+            for (; c < nchunk; ++c) {
                 float d[V];
                 read(c * stride + base, d, -INFINITY);
                 visit(0, d);
