@@ -1343,16 +1343,24 @@ int launch_loop_cache(const Args &a, const Launch &l) {
 
 // LDS-kept chunks of bfloat16 rows go straight from memory to LDS when
 // every window start is 16-byte aligned (row pointer aligned, cols a
-// multiple of 8), the row has one input and at most 64 slots are kept in
-// registers (beside 96 the issue loop would spill); otherwise they pass
-// through registers. Measured over the 2048x128256, 4096x65536 and
-// 4096x49152 streaming cases: 2-3% faster for bfloat16, while float rows
-// (four times as many 16-byte loads per row) ran 1-2.5% slower that way.
+// multiple of 8), the group has 1024 lanes, the row has one input and 32 or
+// 64 slots are kept in registers (beside 96 the issue loop would spill);
+// otherwise they pass through registers. Measured over the 2048x128256,
+// 4096x65536 and 4096x49152 streaming cases: 2-3% faster for bfloat16, while
+// float rows (four times as many 16-byte loads per row) ran 1-2.5% slower
+// that way. LDS then holds the raw 16-byte packs, half the bytes of the
+// widened floats the register route stores, so kDmaChunks of them (144 KiB
+// of the 160 KiB a workgroup may allocate) fit where 4 widened ones did;
+// that also lets RMSNorm's 64-slot plan (alone on its compute unit by its
+// registers, which leave no room for the register route) keep chunks in
+// LDS.
+constexpr int kDmaChunks = 9;
 template <int OP, int V, int KEEP, int LDSC, class T>
 int launch_loop_keep(const Args &a, const Launch &l) {
-    if constexpr (is_bf16<T> && LDSC > 0 && V == 8 && OP != kResidualLayerNorm && KEEP * V <= 64) {
-        if ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0 && a.cols % V == 0)
-            return launch_loop_cache<OP, V, KEEP, LDSC, T, true>(a, l);
+    if constexpr (is_bf16<T> && V == 8 && KEEP > 0 && KEEP * V <= 64 && OP != kResidualLayerNorm &&
+                  (LDSC > 0 || (OP == kRmsNorm && KEEP * V == 64))) {
+        if (l.block.x == 1024 && (reinterpret_cast<uintptr_t>(a.x) & 15) == 0 && a.cols % V == 0)
+            return launch_loop_cache<OP, V, KEEP, kDmaChunks, T, true>(a, l);
     }
     return launch_loop_cache<OP, V, KEEP, LDSC, T, false>(a, l);
 }

@@ -76,6 +76,22 @@ def parse_key(key: str) -> dict:
     return {"path": PATHS[m.group(1)], "block": b, "lanes": w, "v": v, "slots": k, "cache": c}
 
 
+def lds_slots(base: str, bf: bool, p: dict) -> int:
+    """Values per lane a streaming plan also keeps in LDS between its passes:
+    bfloat16 16-byte packs go there raw (9 chunks of 8) for LayerNorm at 32
+    register slots and RMSNorm and softmax at 64; otherwise widened floats
+    (32 per lane) for the LayerNorms at 32 slots and softmax at 64 or 96; all
+    only in 1024-lane groups."""
+    B, V, K = p["block"], p["v"], p["slots"]
+    if p["path"] != 2 or B != 1024 or K == 0:
+        return 0
+    if bf and V == 8 and ((K == 32 and base == "layernorm") or (K == 64 and base in ("rmsnorm", "softmax"))):
+        return 9 * 8
+    if (K == 32 and base in ("layernorm", "residual_layernorm")) or (K in (64, 96) and base == "softmax"):
+        return 32
+    return 0
+
+
 def features(op: str, rows: int, cols: int, p: dict) -> dict:
     """Integer-derived quantities of one launch (all paths of the model)."""
     bf = op.endswith("_bf16")
@@ -88,9 +104,10 @@ def features(op: str, rows: int, cols: int, p: dict) -> dict:
     nw = B // 64
     if path == 2:
         nch = -(-cols // (W * V))
-        kept_cols = min(cols, W * K)
+        held = K + lds_slots(base, bf, p)
+        kept_cols = min(cols, W * held)
         vgpr = 24 + 1.2 * K + 2 * V
-        loads = nch * (n_in * passes + n_w) - min(K // V, nch) * n_in * (passes - 1)
+        loads = nch * (n_in * passes + n_w) - min(held // V, nch) * n_in * (passes - 1)
         elems = nch * V * passes
         exact = False
     else:

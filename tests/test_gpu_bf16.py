@@ -257,14 +257,16 @@ def test_bf16_masked_entries_every_plan(gpu_device, op, cols):
 
 
 @pytest.mark.parametrize("op,slots,cols", [
-    ("layernorm", 32, 32776), ("layernorm", 32, 49152), ("layernorm", 32, 65536), ("layernorm", 32, 98312),
-    ("softmax", 64, 65544), ("softmax", 64, 90000), ("softmax", 64, 131072)])
+    ("layernorm", 32, 32776), ("layernorm", 32, 65536), ("layernorm", 32, 106496), ("layernorm", 32, 128256),
+    ("softmax", 64, 65544), ("softmax", 64, 131072), ("softmax", 64, 139264), ("softmax", 64, 140000),
+    ("rmsnorm", 64, 65536), ("rmsnorm", 64, 65544), ("rmsnorm", 64, 139264), ("rmsnorm", 64, 150000)])
 def test_bf16_lds_kept_chunks(gpu_device, op, slots, cols):
     """1024-lane streaming plans whose chunks past the register-kept ones go
-    to LDS (for 16-byte bfloat16 packs straight from memory): the first
-    LDS chunk partly filled, LDS full, and chunks streamed past it; one row
-    offset by a large mean (LayerNorm statistics of shifted values), one
-    ramp, the rest the standard recipe."""
+    to LDS (16-byte bfloat16 packs straight from memory, 9 chunks of 8192
+    columns beside 4 or 8 in registers): no LDS chunk, the first one partly
+    filled, LDS exactly full, and chunks streamed past it; one row offset by
+    a large mean (LayerNorm statistics of shifted values), one ramp, the
+    rest the standard recipe."""
     rows = 4
     d = host_bf16(rows, cols, seed=500 + cols)
     xf = oracle.bf16_to_float(d["x"]).astype(np.float32)
