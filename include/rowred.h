@@ -129,9 +129,10 @@ typedef enum rr_path {
  *                   v >= 4 and 1024-lane groups also 64 (RMSNorm, softmax)
  *                   and 96 (softmax). 1024-lane softmax plans keeping 64
  *                   or 96, and LayerNorm plans keeping 32, hold 32 more
- *                   values per lane in LDS; with v = 8 bfloat16 rows,
- *                   LayerNorm at 32 and RMSNorm and softmax at 64 hold 72
- *                   more there instead (the raw 16-byte packs).
+ *                   values per lane in LDS; for bfloat16 rows LayerNorm
+ *                   and residual LayerNorm at 32 and softmax at 64 hold 72
+ *                   there instead (as bfloat16), and so does RMSNorm at 64
+ *                   with v = 8.
  *   cache           cache policy for the row data: 0 = default; 1 = output
  *                   stores non-temporal; 2 = row loads (x, residual) and
  *                   output stores non-temporal (on the LOOP path only the

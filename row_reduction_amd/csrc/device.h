@@ -626,8 +626,39 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
     // 16-byte aligned, and one input row (not residual LayerNorm).
     static_assert(!DMA || (LDSC > 0 && V * sizeof(T) == 16 && OP != kResidualLayerNorm && KEEP * V <= 64),
                   "direct-to-LDS chunks: 16-byte packs of one input, at most 64 kept slots");
-    __shared__ float lds_keep[(LDSC > 0 && !DMA) ? LDSC * V * 1024 : 1];
+    // Register route: bfloat16 rows beside at most 64 register slots keep
+    // these chunks as bfloat16 pairs, one 32-bit word per two values
+    // (lossless: what is kept, x or h = bf16(x + residual), and the fill
+    // values are bfloat16 numbers); float rows, and softmax beside 96 slots
+    // (whose instance would spill with the packing), keep floats.
+    constexpr bool kPacked = is_bf16<T> && !DMA && KEEP * V <= 64;
+    __shared__ float lds_keep[(LDSC > 0 && !DMA && !kPacked) ? LDSC * V * 1024 : 1];
+    __shared__ u32 lds_pk[(LDSC > 0 && kPacked) ? LDSC * (V / 2) * 1024 : 1];
     __shared__ u32x4 lds_dma[(LDSC > 0 && DMA) ? LDSC * 1024 : 1];
+    static_assert(LDSC * V * (is_bf16<T> ? 2 : 4) * 1024 <= 144 * 1024, "LDS-kept chunks: at most 144 KiB");
+    auto lds_put = [&](int c, const float *d) {
+        if constexpr (kPacked) {
+#pragma unroll
+            for (int e = 0; e < V / 2; ++e)
+                lds_pk[((c - KEEP) * (V / 2) + e) * 1024 + threadIdx.x] = pack_bf16(d[2 * e], d[2 * e + 1]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) lds_keep[((c - KEEP) * V + e) * 1024 + threadIdx.x] = d[e];
+        }
+    };
+    auto lds_get = [&](int c, float *d) {
+        if constexpr (kPacked) {
+#pragma unroll
+            for (int e = 0; e < V / 2; ++e) {
+                const u32 u = lds_pk[((c - KEEP) * (V / 2) + e) * 1024 + threadIdx.x];
+                d[2 * e] = bf16_lo(u);
+                d[2 * e + 1] = bf16_hi(u);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) d[e] = lds_keep[((c - KEEP) * V + e) * 1024 + threadIdx.x];
+        }
+    };
     const int ldsc = LDSC < nchunk - KEEP ? LDSC : (nchunk - KEEP > 0 ? nchunk - KEEP : 0);
 
     // Pack of the row's values (x, or x + residual for residual LayerNorm).
@@ -750,8 +781,7 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
 #pragma unroll
                 for (int j = 0; j < kLdsBatch; ++j) {
                     visit((c + j) * stride + base, d[j]);
-#pragma unroll
-                    for (int e = 0; e < V; ++e) lds_keep[((c + j - KEEP) * V + e) * 1024 + threadIdx.x] = d[j][e];
+                    lds_put(c + j, d[j]);
                 }
             }
         }
@@ -759,8 +789,7 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
             float d[V];
             read_first(c * stride + base, d, fill);
             visit(c * stride + base, d);
-#pragma unroll
-            for (int e = 0; e < V; ++e) lds_keep[((c - KEEP) * V + e) * 1024 + threadIdx.x] = d[e];
+            lds_put(c, d);
         }
     };
     // Softmax's first pass: the kept chunks are loaded into `keep` and handed
@@ -805,8 +834,7 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
             if constexpr (DMA) {
                 dma_read(c, d, fill);
             } else {
-#pragma unroll
-                for (int e = 0; e < V; ++e) d[e] = lds_keep[((c - KEEP) * V + e) * 1024 + threadIdx.x];
+                lds_get(c, d);
             }
             emit(c * stride + base, d);
         }
@@ -827,8 +855,7 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
             if constexpr (DMA) {
                 dma_read(c, d, fill);
             } else {
-#pragma unroll
-                for (int e = 0; e < V; ++e) d[e] = lds_keep[((c - KEEP) * V + e) * 1024 + threadIdx.x];
+                lds_get(c, d);
             }
             emit(c * stride + base, d);
         }
@@ -1371,24 +1398,33 @@ int launch_loop_keep(const Args &a, const Launch &l) {
 // workgroup without spilling (the LayerNorms would spill at 64). A 1024-lane
 // plan whose registers are full that way (softmax at 64 or 96 slots, the
 // LayerNorms at 32) runs one workgroup per compute unit anyway, so it also
-// keeps the next 32 slots per lane in LDS (128 KiB): a 65536-column float
-// LayerNorm row, or 131072 columns of softmax (a 128256-entry vocabulary),
-// is then read once. (RMSNorm at 64 slots already holds a 65536-column row;
-// with LDS added its instance would spill.)
+// keeps the next values of each lane in LDS: 32 floats (128 KiB), or 72
+// bfloat16 values (144 KiB; 32 beside softmax's 96 slots): a 65536-column
+// float LayerNorm row, or 131072 columns of softmax (a 128256-entry
+// vocabulary), is then read once.
+// (Float RMSNorm at 64 slots already holds a 65536-column row; with LDS
+// added its instance would spill. bfloat16 RMSNorm at 64 slots takes 72
+// values per lane into LDS straight from memory.)
 template <int OP, int V, class T>
 int launch_loop(int slots, const Args &a, const Launch &l) {
     if (slots == 0) return launch_loop_keep<OP, V, 0, 0, T>(a, l);
     constexpr bool kLn = OP == kLayerNorm || OP == kResidualLayerNorm;
+    // LDS-kept chunks: 32 float values per lane (128 KiB), or 72 bfloat16
+    // values (144 KiB) for bfloat16 rows.
+    constexpr int kLds = (is_bf16<T> ? 72 : 32) / V;
     if constexpr (V >= 4 && OP != kSum && OP != kCrossEntropy) {
         if (slots == 32) {
-            if (kLn && l.block.x == 1024) return launch_loop_keep<OP, V, 32 / V, (kLn ? 32 / V : 0), T>(a, l);
+            if (kLn && l.block.x == 1024) return launch_loop_keep<OP, V, 32 / V, (kLn ? kLds : 0), T>(a, l);
             return launch_loop_keep<OP, V, 32 / V, 0, T>(a, l);
         }
     }
     if constexpr (V >= 4 && (OP == kRmsNorm || OP == kSoftmax)) {
-        if (slots == 64) return launch_loop_keep<OP, V, 64 / V, (OP == kSoftmax ? 32 / V : 0), T>(a, l);
+        if (slots == 64) return launch_loop_keep<OP, V, 64 / V, (OP == kSoftmax ? kLds : 0), T>(a, l);
     }
     if constexpr (V >= 4 && OP == kSoftmax) {
+        // Beside 96 register slots the LDS chunks are loaded one at a time
+        // (no registers to batch them), so more of them gained nothing; they
+        // hold 32 values per lane.
         if (slots == 96) return launch_loop_keep<OP, V, 96 / V, 32 / V, T>(a, l);
     }
     return (int)hipErrorInvalidValue;

@@ -77,18 +77,20 @@ def parse_key(key: str) -> dict:
 
 
 def lds_slots(base: str, bf: bool, p: dict) -> int:
-    """Values per lane a streaming plan also keeps in LDS between its passes:
-    bfloat16 16-byte packs go there raw (9 chunks of 8) for LayerNorm at 32
-    register slots and RMSNorm and softmax at 64; otherwise widened floats
-    (32 per lane) for the LayerNorms at 32 slots and softmax at 64 or 96; all
-    only in 1024-lane groups."""
+    """Values per lane a streaming plan also keeps in LDS between its passes,
+    as the kernels do (1024-lane groups only): the LayerNorms at 32 register
+    slots and softmax at 64 keep 32 floats per lane, or 72 bfloat16 values
+    for bfloat16 rows; softmax at 96 keeps 32; bfloat16 RMSNorm at 64 slots
+    with v = 8 keeps 72."""
     B, V, K = p["block"], p["v"], p["slots"]
     if p["path"] != 2 or B != 1024 or K == 0:
         return 0
-    if bf and V == 8 and ((K == 32 and base == "layernorm") or (K == 64 and base in ("rmsnorm", "softmax"))):
-        return 9 * 8
-    if (K == 32 and base in ("layernorm", "residual_layernorm")) or (K in (64, 96) and base == "softmax"):
+    if K == 96 and base == "softmax":
         return 32
+    if (K == 32 and base in ("layernorm", "residual_layernorm")) or (K == 64 and base == "softmax"):
+        return 72 if bf else 32
+    if bf and V == 8 and K == 64 and base == "rmsnorm":
+        return 72
     return 0
 
 

@@ -256,17 +256,22 @@ def test_bf16_masked_entries_every_plan(gpu_device, op, cols):
         compare(got, ref, what)
 
 
-@pytest.mark.parametrize("op,slots,cols", [
-    ("layernorm", 32, 32776), ("layernorm", 32, 65536), ("layernorm", 32, 106496), ("layernorm", 32, 128256),
-    ("softmax", 64, 65544), ("softmax", 64, 131072), ("softmax", 64, 139264), ("softmax", 64, 140000),
-    ("rmsnorm", 64, 65536), ("rmsnorm", 64, 65544), ("rmsnorm", 64, 139264), ("rmsnorm", 64, 150000)])
-def test_bf16_lds_kept_chunks(gpu_device, op, slots, cols):
-    """1024-lane streaming plans whose chunks past the register-kept ones go
-    to LDS (16-byte bfloat16 packs straight from memory, 9 chunks of 8192
-    columns beside 4 or 8 in registers): no LDS chunk, the first one partly
-    filled, LDS exactly full, and chunks streamed past it; one row offset by
-    a large mean (LayerNorm statistics of shifted values), one ramp, the
-    rest the standard recipe."""
+@pytest.mark.parametrize("op,v,slots,cols", [
+    ("layernorm", 8, 32, 32776), ("layernorm", 8, 32, 65536), ("layernorm", 8, 32, 106496), ("layernorm", 8, 32, 128256),
+    ("layernorm", 4, 32, 32776), ("layernorm", 4, 32, 106496), ("layernorm", 4, 32, 110000),
+    ("residual_layernorm", 8, 32, 32776), ("residual_layernorm", 8, 32, 106496), ("residual_layernorm", 8, 32, 128256),
+    ("softmax", 8, 64, 65544), ("softmax", 8, 64, 131072), ("softmax", 8, 64, 139264), ("softmax", 8, 64, 140000),
+    ("softmax", 8, 96, 98312), ("softmax", 8, 96, 131072), ("softmax", 8, 96, 140000),
+    ("rmsnorm", 8, 64, 65536), ("rmsnorm", 8, 64, 65544), ("rmsnorm", 8, 64, 139264), ("rmsnorm", 8, 64, 150000)])
+def test_bf16_lds_kept_chunks(gpu_device, op, v, slots, cols):
+    """1024-lane streaming plans that keep values past the register-kept ones
+    in LDS, 72 per lane for bfloat16 rows: raw 16-byte packs loaded straight
+    from memory (v = 8 with one input row) or bfloat16 pairs written from
+    registers (residual LayerNorm's h, v = 4; 32 beside softmax's 96
+    register slots). Shapes with no LDS chunk, the first one partly filled, LDS
+    exactly full, and chunks streamed past it; one row offset by a large
+    mean (LayerNorm statistics of shifted values), one ramp, the rest the
+    standard recipe."""
     rows = 4
     d = host_bf16(rows, cols, seed=500 + cols)
     xf = oracle.bf16_to_float(d["x"]).astype(np.float32)
@@ -275,8 +280,8 @@ def test_bf16_lds_kept_chunks(gpu_device, op, slots, cols):
     d["x"] = workloads.as_bf16_bits(xf)
     ref = run_oracle(op, d, eps_of(op))
     t = dev_inputs(d, gpu_device)
-    p = rr.rr_plan(2, 1024, 1024, 1, 8, slots, 2)
+    p = rr.rr_plan(2, 1024, 1024, 1, v, slots, 2)
     assert rr.rr_check_plan(op + "_bf16", rows, cols, p) == 0
-    what = f"lds-kept {op}_bf16 {rows}x{cols} k{slots}"
+    what = f"lds-kept {op}_bf16 {rows}x{cols} v{v} k{slots}"
     announce(what)
     compare(run_gpu(op, t, eps_of(op), plan=p), ref, what)
