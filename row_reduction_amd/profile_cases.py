@@ -161,7 +161,9 @@ def demangle(name: str) -> str:
     order; bfloat16 shown as bf16), whether or not the trace demangled it."""
     import re
     if not name.startswith("_Z"):
-        return name
+        # The profiler's own demangling reads a bfloat16 argument followed by
+        # `true` (DF16bLb1E) as these three.
+        return name.replace("bool _Accum, bool, E>", "bf16, true>")
     m = re.match(r"_ZN6rowred(\d+)(\w+?)I(.*)EEvNS_4ArgsE$", name)
     if not m:
         return name
