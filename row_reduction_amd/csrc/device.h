@@ -635,7 +635,8 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
     __shared__ float lds_keep[(LDSC > 0 && !DMA && !kPacked) ? LDSC * V * 1024 : 1];
     __shared__ u32 lds_pk[(LDSC > 0 && kPacked) ? LDSC * (V / 2) * 1024 : 1];
     __shared__ u32x4 lds_dma[(LDSC > 0 && DMA) ? LDSC * 1024 : 1];
-    static_assert(LDSC * V * (is_bf16<T> ? 2 : 4) * 1024 <= 144 * 1024, "LDS-kept chunks: at most 144 KiB");
+    static_assert(LDSC * 1024 * (DMA ? 16 : kPacked ? 2 * V : 4 * V) <= 144 * 1024,
+                  "LDS-kept chunks: at most 144 KiB");
     auto lds_put = [&](int c, const float *d) {
         if constexpr (kPacked) {
 #pragma unroll
