@@ -37,6 +37,27 @@ def test_cpp_model_equals_python_reference(cases, theta):
     assert worst <= 1e-12
 
 
+@pytest.mark.parametrize("op", OPS)
+def test_cpp_model_equals_python_reference_on_long_rows(op, theta):
+    """The same agreement on rows past the register budget, where the
+    streaming plans' LDS-held columns count as kept: every legal streaming
+    candidate of three long shapes, with at least one holding values in LDS
+    for the operators that can."""
+    held = 0
+    for rows, cols in ((256, 50257), (2048, 128256), (300, 200000)):
+        for p in plans.candidate_plans(op, rows, cols, caches=(2,)):
+            d = pm.parse_key(plans.plan_key(p))
+            if d["path"] != 2:
+                continue
+            bf = op.endswith("_bf16")
+            held += pm.lds_slots(op[:-5] if bf else op, bf, d) > 0
+            got = rr.rr_model_time_us(op, rows, cols, p)
+            want = pm.predict_us(pm.features(op, rows, cols, d), theta)
+            assert abs(got - want) <= 1e-12 * want, (op, rows, cols, plans.plan_key(p))
+    holds_lds = op.split("_bf16")[0] in ("softmax", "layernorm", "residual_layernorm") or op == "rmsnorm_bf16"
+    assert (held > 0) == holds_lds
+
+
 def model_cache(op, rows, cols):
     e = 2 if op.endswith("_bf16") else 4
     k = 3 if op.startswith("residual") else 2
