@@ -570,15 +570,17 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
     }
 }
 
-// The row's first value h0 (x, or x + residual at the tensors' precision),
-// read by every lane: the shift of the LayerNorms' float64 sums.
+// The value h (x, or x + residual at the tensors' precision) at flat position
+// `pos`, read by every lane: the shift of the LayerNorms' sums (the row's
+// first value on the streaming path, the slice's first value on the split
+// path).
 template <int OP, class T>
-__device__ __forceinline__ float row_first_value(const Args &a, int64_t off) {
+__device__ __forceinline__ float value_at(const Args &a, int64_t pos) {
     float h0;
-    load_pack<1>(static_cast<const T *>(a.x) + off, &h0);
+    load_pack<1>(static_cast<const T *>(a.x) + pos, &h0);
     if constexpr (OP == kResidualLayerNorm) {
         float r0;
-        load_pack<1>(static_cast<const T *>(a.residual) + off, &r0);
+        load_pack<1>(static_cast<const T *>(a.residual) + pos, &r0);
         h0 = is_bf16<T> ? round_to_bf16(h0 + r0) : h0 + r0;
     }
     return h0;
@@ -1011,7 +1013,7 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
         // sqrt(var + eps) amplifies.) Chan's weights k / (n + k) use the
         // hardware reciprocal: a 1-ulp error in a weight moves the merged
         // mean and M2 by far less than their own rounding.
-        const float h0 = row_first_value<OP, T>(a, off);
+        const float h0 = value_at<OP, T>(a, off);
         float n = 0.0f, mean = 0.0f, m2 = 0.0f;
         double sum = 0.0;
         // One pack: its values' shifted mean and M2 merged into the lane's
@@ -1085,8 +1087,13 @@ __global__ void __launch_bounds__(1024) loop_kernel(const Args a) {
 // slice and writes the outputs. Partials:
 //   RMSNorm: (sum x^2, -)          row sum: (sum x, -)
 //   softmax / cross-entropy: (slice max m, sum exp(x - m))
-//   LayerNorm: (sum (h - h0), sum (h - h0)^2) in float64, h0 the row's first
-//   value, which every slice reads; merged by plain sums in slice order.
+//   LayerNorm: the slice's mean and M2 = sum (h - mean)^2, in float64, from
+//   sums of h - c shifted by the slice's own first value c (so they round at
+//   the scale of the row's spread, not of its mean); merged with Chan's
+//   formula for combining (count, mean, M2) groups. The second launch reads
+//   no input outside its own slice, so y may alias x: a shift shared by the
+//   whole row would have to be re-read from x[row, 0], which the slice-0
+//   workgroup of that launch may already have overwritten.
 
 struct Partial2 {
     double a, b;
@@ -1178,28 +1185,33 @@ __global__ void __launch_bounds__(1024) split_partial_kernel(const Args a) {
         out.b = (double)row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds1);
     } else {
         static_assert(OP == kLayerNorm || OP == kResidualLayerNorm, "unknown operator");
-        const double h0 = (double)row_first_value<OP, T>(a, off);
+        // Inputs are not written during this launch (h_out may not alias
+        // them), so the slice's first value reads the same in every lane.
+        const double c0 = (double)value_at<OP, T>(a, off + first);
         double s1 = 0.0, s2 = 0.0;
 #pragma unroll
         for (int c = 0; c < NCHUNK; ++c) {
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const int i0 = c * stride + base, j = window_start<V>(i0, cols) + e;
-                const double dd = (j >= i0 && j < end) ? (double)v[c * V + e] - h0 : 0.0;
+                const double dd = (j >= i0 && j < end) ? (double)v[c * V + e] - c0 : 0.0;
                 s1 += dd;
                 s2 += dd * dd;
             }
         }
-        out.a = row_reduce(s1, AddOp{}, rl, ldsd);
-        out.b = row_reduce(s2, AddOp{}, rl, ldsd2);
+        const double S1 = row_reduce(s1, AddOp{}, rl, ldsd);
+        const double S2 = row_reduce(s2, AddOp{}, rl, ldsd2);
+        const double n = (double)(end - first);
+        out.a = c0 + S1 / n;                   // slice mean
+        out.b = fmax(0.0, S2 - S1 * (S1 / n));  // slice M2
     }
     if (threadIdx.x == 0) static_cast<Partial2 *>(a.workspace)[row * gridDim.x + s] = out;
 }
 
-// Merge of the row's `slices` partials, each lane taking every W-th one in
-// slice order, then the fixed-order row reduction.
+// Merge of the row's `slices` partials (slices of `span` columns), each lane
+// taking every W-th one in slice order, then the fixed-order row reduction.
 template <int OP>
-__device__ __forceinline__ void merge_partials(const Partial2 *p, int slices, int cols, double h0,
+__device__ __forceinline__ void merge_partials(const Partial2 *p, int slices, int span, int cols,
                                                const RowLanes<64> &rl, double *ldsd0, double *ldsd1,
                                                double &stat0, double &stat1) {
     if constexpr (OP == kRmsNorm || OP == kSum) {
@@ -1216,16 +1228,18 @@ __device__ __forceinline__ void merge_partials(const Partial2 *p, int slices, in
         stat0 = m;
         stat1 = row_reduce(z, AddOp{}, rl, ldsd1);
     } else {
-        // Shifted sums: mean = h0 + S1 / n, var = (S2 - S1^2 / n) / n.
-        double a1 = 0.0, a2 = 0.0;
+        // Chan's merge of (n_j, mean_j, M2_j): mean = sum n_j mean_j / n,
+        // M2 = sum (M2_j + n_j (mean_j - mean)^2); var = M2 / n.
+        double a1 = 0.0;
+        for (int j = rl.lane; j < slices; j += rl.W) a1 += (double)slice_len(j, span, cols) * p[j].a;
+        const double mean = row_reduce(a1, AddOp{}, rl, ldsd0) / (double)cols;
+        double a2 = 0.0;
         for (int j = rl.lane; j < slices; j += rl.W) {
-            a1 += p[j].a;
-            a2 += p[j].b;
+            const double d = p[j].a - mean;
+            a2 += p[j].b + (double)slice_len(j, span, cols) * d * d;
         }
-        const double S1 = row_reduce(a1, AddOp{}, rl, ldsd0);
-        const double S2 = row_reduce(a2, AddOp{}, rl, ldsd1);
-        stat0 = h0 + S1 / (double)cols;
-        stat1 = fmax(0.0, (S2 - S1 * (S1 / (double)cols)) / (double)cols);
+        stat0 = mean;
+        stat1 = row_reduce(a2, AddOp{}, rl, ldsd1) / (double)cols;
     }
 }
 
@@ -1247,9 +1261,7 @@ __global__ void __launch_bounds__(1024) split_final_kernel(const Args a) {
     const int end = first + slice_len(s, span, cols);
     const Partial2 *p = static_cast<const Partial2 *>(a.workspace) + row * slices;
     double stat0 = 0.0, stat1 = 0.0;
-    double h0 = 0.0;
-    if constexpr (OP == kLayerNorm || OP == kResidualLayerNorm) h0 = (double)row_first_value<OP, T>(a, off);
-    merge_partials<OP>(p, slices, cols, h0, rl, ldsd0, ldsd1, stat0, stat1);
+    merge_partials<OP>(p, slices, span, cols, rl, ldsd0, ldsd1, stat0, stat1);
 
     const T *xr = static_cast<const T *>(a.x) + off;
     if constexpr (OP == kSum) {

@@ -133,16 +133,64 @@ def test_split_deterministic_and_workspace_reuse(gpu_device):
             "split rmsnorm 2x50000 reused workspace")
 
 
-def test_split_in_place_rmsnorm(gpu_device):
-    """y aliasing x is safe for split rows: each slice's final workgroup
-    re-reads only its own columns before storing them."""
+IN_PLACE_OPS = ["rmsnorm", "softmax", "layernorm", "residual_layernorm"]
+
+
+def run_in_place(op, t, plan, ws, bf16):
+    """One call with y aliasing x (residual LayerNorm: h_out in its own buffer)."""
     import torch
-    d = family_host_inputs("rmsnorm", 3, 100003, seed=7)
-    ref = oracle.rmsnorm(d["x"], d["w"], d["eps"])
-    x = torch.from_numpy(d["x"]).to(gpu_device)
-    w = torch.from_numpy(d["w"]).to(gpu_device)
-    ws = torch.empty(rr.rr_workspace_bytes("rmsnorm", 3, 100003), dtype=torch.uint8, device=gpu_device)
-    announce("split rmsnorm in place")
-    rr.rmsnorm_f32(x, w, d["eps"], y=x, workspace=ws)
-    from parity_util import assert_close
-    assert_close(x.cpu().numpy(), ref, "split in place")
+    eps = t["eps"]
+    x = t["x"]
+    sfx = "_bf16" if bf16 else "_f32"
+    if op == "rmsnorm":
+        getattr(rr, "rmsnorm" + sfx)(x, t["w"], eps, y=x, plan=plan, workspace=ws)
+        return {"y": x}
+    if op == "softmax":
+        getattr(rr, "softmax" + sfx)(x, y=x, plan=plan, workspace=ws)
+        return {"y": x}
+    if op == "layernorm":
+        getattr(rr, "layernorm" + sfx)(x, t["w"], t["beta"], eps, y=x, plan=plan, workspace=ws)
+        return {"y": x}
+    h = torch.empty_like(x)
+    getattr(rr, "residual_layernorm" + sfx)(x, t["residual"], t["w"], t["beta"], eps, y=x, h_out=h,
+                                           plan=plan, workspace=ws)
+    return {"y": x, "h": h}
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+@pytest.mark.parametrize("op", IN_PLACE_OPS)
+def test_split_in_place(gpu_device, op, bf16):
+    """y aliasing x is safe on split rows for every per-element operator: the
+    second launch's workgroups read only their own slice's columns (the
+    LayerNorms' shift is each slice's own first value, taken in the first
+    launch, which writes no input), for every explicit split plan and the
+    selected one, with slices that finish at different times (many rows,
+    narrow slices)."""
+    import torch
+    rows, cols = 5, 100000
+    name = op + ("_bf16" if bf16 else "")
+    if bf16:
+        d = workloads.family_inputs_bf16(rows, cols, seed=11)
+        eps = workloads.RMSNORM_EPS if op == "rmsnorm" else workloads.LAYERNORM_EPS
+        ref = run_oracle_bf16(op, d, eps)
+        fresh = lambda: dict(dev_inputs_bf16(d, gpu_device), w=None, eps=eps)
+    else:
+        d = family_host_inputs(op, rows, cols, seed=11)
+        ref = run_oracle(op, d)
+        fresh = lambda: {k: (torch.from_numpy(np.ascontiguousarray(v)).to(gpu_device)
+                             if isinstance(v, np.ndarray) else v) for k, v in d.items()}
+    plans = [None] + split_plans(name, rows, cols)
+    assert len(plans) >= 4
+    for p in plans:
+        t = fresh()
+        if bf16:
+            t["w"] = t["gamma"]
+        need = rr.rr_workspace_bytes(name, rows, cols, p)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=gpu_device)
+        what = f"split {name} {rows}x{cols} in place " + (f"w{p.lanes_per_row} k{p.slots}" if p else "selected")
+        announce(what)
+        got = run_in_place(op, t, p, ws, bf16)
+        if bf16:
+            compare_bf16(got, ref, what)
+        else:
+            compare(op, got, ref, what)
