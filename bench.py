@@ -4,25 +4,39 @@
 One step = one rmsnorm_f32 call (plan lookup, vectorised load, per-lane sum of
 squares, wavefront and LDS reduction, rsqrt-scale epilogue and store) over the
 bandwidth-bound 16384x8192 RMSNorm workload (x ~ N(0,1), w ~ U(0.5,1.5),
-eps = 1e-6), inputs resident in HBM. Prints one JSON line:
+eps = 1e-6), inputs resident in HBM.
 
-  value      whole-job throughput of the timed steps in algorithmic GB/s
-             (bytes = 8*rows*cols + 4*cols per call: x read once, y written
-             once, w read once)
-  roofline   the RMSNorm kernel's achieved GB/s (algorithmic bytes / average
-             kernel duration from HIP events on the launch stream) against
-             MI355X's 8 TB/s HBM peak; `traffic` from hardware counters when
-             a committed counter summary matches the current kernel source
+The LAST line on stdout is one compact JSON object (under 2 KB):
+
+  value         whole-job throughput of the timed steps in algorithmic GB/s
+                (bytes = 8*rows*cols + 4*cols per call: x read once, y
+                written once, w read once)
+  roofline      the RMSNorm kernel's achieved GB/s (algorithmic bytes /
+                average kernel duration from HIP events on the launch stream)
+                against MI355X's 8 TB/s HBM peak; `traffic` from hardware
+                counters when a committed counter summary matches the current
+                kernel source
   cpu_baseline  the CPU oracle timed on host cores over a bounded sample
-  shapes     per-shape us/op, rows/s, GB/s and fraction of peak for every
-             measured RMSNorm shape and the five sibling operators, next to
-             an empty-kernel launch floor and a same-bytes copy ceiling
-  long_rows  few long rows: one workgroup per row against split rows
+  parity        how many timed configurations were checked in full against
+                the oracle in this run, and how many failed
+
+Everything else goes to a detail file (--detail, default
+gpurun_out/bench_detail.json) and, one line per row, to stderr:
+
+  shapes          per (operator, shape, cache state): GPU us/op (median of
+                  graph-replayed samples, raw samples kept), rows/s, GB/s and
+                  fraction of peak; the fastest same-bytes stream (copy, or
+                  read-only for row sum and cross-entropy) over 12 geometries;
+                  the CPU oracle's us/op on the same inputs (all cores used
+                  and one core), the GPU/oracle speedup, and a full
+                  element-by-element check of the GPU output against the
+                  oracle taken before the row is timed
+  long_rows       few long rows: one workgroup per row against split rows
   streaming_rows  many rows beyond the register path (vocabulary-size
-             cross-entropy and softmax, 65536-column normalisations)
-  single_call  end-to-end latency of one tiny call (C entry point and
-             binding), and the 24-call operator-coverage set as separate
-             launches against one batched launch
+                  cross-entropy and softmax, 65536-column normalisations)
+  single_call     end-to-end latency of one tiny call, and the 24-call
+                  operator-coverage set as separate launches against one
+                  batched launch
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-shapes] [--no-cpu]
 """
@@ -43,7 +57,10 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0
 METRIC = "FP32 RMSNorm µs/op + achieved HBM GB/s (% of MI355X peak) per shape"
 HEADLINE = (16384, 8192)
-COLD_SET_BYTES = 768 << 20  # distinct buffers cycled for cache-cold timings
+# Host threads the CPU oracle may use: the host cores this process may run on,
+# capped at 16, a one-GPU share of the GPU host's cores.
+CPU_THREAD_CAP = 16
+STREAM_GEOMETRIES = [(p, b) for p in (1, 2, 4, 8) for b in (256, 512, 1024)]
 
 
 def log(msg: str) -> None:
@@ -55,6 +72,12 @@ def kernel_source_hash() -> str:
     and the selected plan (the counter summary records the same)."""
     from row_reduction_amd.profile_cases import headline_fingerprint
     return headline_fingerprint()
+
+
+def device_source_hash() -> str:
+    """sha256 of every device source (what any row's timing depends on)."""
+    from row_reduction_amd.tune import source_hash
+    return source_hash()
 
 
 def counter_traffic(source_hash: str):
@@ -88,24 +111,6 @@ class Timer:
         return self.start.elapsed_time(self.stop)
 
 
-def batch_us(torch, fn, target_ms: float = 20.0, rounds: int = 3, samples: int = 5) -> dict:
-    """Median of per-round medians of batch-amortised microseconds per call."""
-    timer = Timer(torch)
-    fn()
-    torch.cuda.synchronize()
-    probe = timer.time_ms(fn, 5) / 5
-    n = max(5, min(20000, int(target_ms / max(probe, 1e-3))))
-    per_round = []
-    raw = []
-    for _ in range(rounds):
-        vals = sorted(timer.time_ms(fn, n) * 1000.0 / n for _ in range(samples))
-        raw.extend(vals)
-        per_round.append(vals[len(vals) // 2])
-    per_round.sort()
-    return {"us": per_round[len(per_round) // 2], "min_us": min(raw), "max_us": max(raw),
-            "launches_per_sample": n}
-
-
 def graph_us(torch, fn, n: int, samples: int = 15) -> dict:
     """Median us per call over replays of a HIP graph of n calls of fn."""
     fn()
@@ -117,85 +122,9 @@ def graph_us(torch, fn, n: int, samples: int = 15) -> dict:
     timer = Timer(torch)
     g.replay()
     torch.cuda.synchronize()
-    vals = sorted(timer.time_ms(g.replay, 1) * 1000.0 / n for _ in range(samples))
-    return {"us": vals[len(vals) // 2], "min_us": vals[0], "max_us": vals[-1]}
-
-
-def shape_table(torch, rr, workloads, device, samples: int = 15) -> list:
-    """us/op and GB/s for every measured shape and operator with the selected
-    plan. Each sample replays a HIP graph of back-to-back launches (GPU time
-    per call, host launch cost excluded); working sets of 1 MiB or more are
-    also timed cold, cycling >= 768 MiB of distinct buffers. `single_call_us`
-    is one synchronised host call, launch to completion. `copy_same_shape_*`
-    is rr_copy_f32 over a matrix of the same shape and element size timed the
-    same way: the practical per-call bound at that size."""
-    from row_reduction_amd.tune import COLD_BYTES, Case, GraphTimer, launches_per_graph
-    out = []
-    copy_cache = {}
-
-    def copy_ceiling(rows, cols, cold, elem):
-        """Per-call us of rr_copy_f32 reading and writing a rows x cols matrix
-        of `elem`-byte elements (2 * elem * RC bytes), hot or cycling distinct
-        buffers like the cold cases."""
-        key = (rows, cols, cold, elem)
-        if key not in copy_cache:
-            n = max(1, rows * cols * elem // 4)
-            nsets = max(2, min(1024, COLD_BYTES // (8 * n))) if cold else 1
-            src = [torch.randn(n, device=device) for _ in range(nsets)]
-            dst = [torch.empty(n, device=device) for _ in range(nsets)]
-            it = [0]
-
-            def call():
-                i = it[0] = (it[0] + 1) % nsets
-                rr.rr_copy_f32(src[i], dst[i])
-            reps = max(nsets, 40 if n < (1 << 20) else 8)
-            res = graph_us(torch, call, reps)
-            copy_cache[key] = res["us"]
-            del src, dst
-        return copy_cache[key]
-    pairs = [("rmsnorm", s) for s in [(1, 127), (17, 257), (64, 4096), (1024, 4096)]]
-    pairs += [(op, s) for s in workloads.FAMILY_SHAPES for op in workloads.OPS if op != "rmsnorm"]
-    pairs += [("rmsnorm_bf16", s) for s in [(1, 127), (17, 257), (64, 4096), (1024, 4096), (16384, 8192)]]
-    pairs += [(op + "_bf16", s) for s in workloads.FAMILY_SHAPES for op in workloads.OPS if op != "rmsnorm"]
-    for op, (rows, cols) in pairs:
-        plan = rr.rr_select_plan(op, rows, cols)
-        inherently_cold = False
-        for hot in (True, False):
-            if not hot and inherently_cold:
-                break
-            case = Case(torch, op, rows, cols, False, device, hot=hot)
-            if not hot and not case.cold_possible:
-                continue
-            inherently_cold = hot and case.cold
-            n = launches_per_graph(torch, case, plan)
-            gt = GraphTimer(torch, case, plan, n)
-            vals = sorted(gt.sample_us() for _ in range(samples))
-            us = vals[len(vals) // 2]
-            single = []
-            if hot:
-                for _ in range(21):
-                    torch.cuda.synchronize()
-                    t0 = time.perf_counter()
-                    case.launch(0, plan)
-                    torch.cuda.synchronize()
-                    single.append((time.perf_counter() - t0) * 1e6)
-                single.sort()
-            nbytes = workloads.algorithmic_bytes(op, rows, cols)
-            gbps = nbytes / (us * 1e3)
-            elem = 2 if op.endswith("_bf16") else 4
-            cus = copy_ceiling(rows, cols, case.cold, elem)
-            out.append({"op": op, "shape": f"{rows}x{cols}", "cache": "cold" if case.cold else "hot",
-                        "us_per_op": round(us, 3), "min_us": round(vals[0], 3),
-                        "max_us": round(vals[-1], 3), "launches_per_graph": n,
-                        "rows_per_s": round(rows / (us * 1e-6), 1), "GBps": round(gbps, 1),
-                        "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
-                        "single_call_us": round(single[len(single) // 2], 2) if single else None,
-                        "copy_same_shape_us": round(cus, 3),
-                        "copy_same_shape_GBps": round(2 * elem * rows * cols / (cus * 1e3), 1),
-                        "plan": plan.as_dict()})
-            del gt, case
-            torch.cuda.empty_cache()
-    return out
+    vals = [timer.time_ms(g.replay, 1) * 1000.0 / n for _ in range(samples)]
+    s = sorted(vals)
+    return {"us": s[len(s) // 2], "min_us": s[0], "max_us": s[-1], "samples_us": [round(v, 4) for v in vals]}
 
 
 def device_info(torch) -> dict:
@@ -205,54 +134,364 @@ def device_info(torch) -> dict:
             "compute_units": p.multi_processor_count, "memory_GiB": round(p.total_memory / 2 ** 30, 1)}
 
 
-def host_cores() -> int:
-    """Host cores available to this process (capped at 16, a one-GPU share)."""
+def host_cores() -> tuple[int, int]:
+    """(threads the oracle uses, host cores this process may run on)."""
     try:
         n = len(os.sched_getaffinity(0))
     except (AttributeError, OSError):
         n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    return max(1, min(CPU_THREAD_CAP, n)), n
 
 
-def long_rows_table(torch, rr, device, samples: int = 11) -> list:
+def cpu_model() -> str:
+    cpu = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return cpu
+
+
+# ---- same-bytes stream ceiling ----------------------------------------------------
+
+class Ceilings:
+    """Fastest rr_stream_f32 geometry moving a given number of bytes: a copy
+    (half read, half written) or a read-only stream, hot or cycling distinct
+    buffers like the cold cases; per call, graph-replayed like the rows."""
+
+    def __init__(self, torch, rr, device):
+        self.torch, self.rr, self.device = torch, rr, device
+        self.cache = {}
+
+    def get(self, nbytes: int, read_only: bool, cold: bool) -> dict:
+        from row_reduction_amd.tune import COLD_BYTES
+        torch = self.torch
+        n = max(4, nbytes // (4 if read_only else 8))
+        n = -(-n // 256) * 256 if n >= (1 << 16) else n
+        key = (n, read_only, cold)
+        if key in self.cache:
+            return self.cache[key]
+        per_set = 4 * n * (1 if read_only else 2)
+        nsets = max(2, min(1024, -(-COLD_BYTES // per_set))) if cold else 1
+        src = [torch.zeros(n, device=self.device) for _ in range(nsets)]
+        dst = [torch.empty(n, device=self.device) for _ in range(nsets)]
+        geoms = STREAM_GEOMETRIES if per_set >= (1 << 20) else [(1, 256), (8, 1024)]
+        best = None
+        for packs, block in geoms:
+            it = [0]
+
+            def call(packs=packs, block=block):
+                i = it[0] = (it[0] + 1) % nsets
+                self.rr.rr_stream_f32(src[i], dst[i], copy=not read_only, packs_per_thread=packs, block=block)
+            reps = max(nsets, 40 if per_set < (1 << 22) else 8)
+            res = graph_us(torch, call, reps, samples=7)
+            if best is None or res["us"] < best["us"]:
+                best = {"us": round(res["us"], 3), "packs_per_thread": packs, "block": block,
+                        "kind": "read" if read_only else "copy", "bytes": per_set}
+        best["GBps"] = round(best["bytes"] / (best["us"] * 1e3), 1)
+        del src, dst
+        torch.cuda.empty_cache()
+        self.cache[key] = best
+        return best
+
+
+# ---- the CPU baseline leg: the only part of the benchmark that uses the oracle ----
+
+class OracleLeg:
+    """The CPU oracle as it is (plain fp64 C loops), run on the same seeded
+    inputs as the GPU: over the whole matrix with a static row split on
+    `cores` threads (its result is also the reference for a full check of the
+    GPU output), and on one thread over a row sample scaled to the matrix."""
+
+    def __init__(self, cores: int):
+        import oracle
+        self.oracle = oracle
+        self.cores = cores
+
+    def _fn(self, op: str, h: dict):
+        o = self.oracle
+        bf = op.endswith("_bf16")
+        base = op[:-5] if bf else op
+        sfx = "_bf16" if bf else ""
+        if base == "rmsnorm":
+            f = getattr(o, "rmsnorm" + sfx)
+            return lambda a, b: {"y": f(h["x"][a:b], h["w"], h["eps"])}
+        if base == "sum":
+            f = getattr(o, "row_sum" + sfx)
+            return lambda a, b: {"out": f(h["x"][a:b])}
+        if base == "softmax":
+            f = getattr(o, "softmax" + sfx)
+            return lambda a, b: {"y": f(h["x"][a:b])}
+        if base == "layernorm":
+            f = getattr(o, "layernorm" + sfx)
+            return lambda a, b: {"y": f(h["x"][a:b], h["w"], h["beta"], h["eps"])}
+        if base == "residual_layernorm":
+            f = getattr(o, "residual_layernorm" + sfx)
+            return lambda a, b: {"y": f(h["x"][a:b], h["residual"][a:b], h["w"], h["beta"], h["eps"])[0]}
+        f = getattr(o, "cross_entropy" + sfx)
+        return lambda a, b: {"out": f(h["x"][a:b], h["targets"][a:b])}
+
+    def reference(self, op: str, h: dict, rows: int):
+        """Oracle outputs of the whole matrix and the seconds it took on
+        min(cores, rows) threads (repeated to at least 50 ms, median)."""
+        import concurrent.futures as cf
+
+        import numpy as np
+        fn = self._fn(op, h)
+        threads = max(1, min(self.cores, rows))
+        bounds = [rows * i // threads for i in range(threads + 1)]
+        times, out = [], None
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            t_total = 0.0
+            while not times or (t_total < 0.05 and len(times) < 50):
+                t0 = time.perf_counter()
+                parts = list(ex.map(lambda i: fn(bounds[i], bounds[i + 1]), range(threads)))
+                dt = time.perf_counter() - t0
+                times.append(dt)
+                t_total += dt
+                if out is None:
+                    out = {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
+        times.sort()
+        return out, times[len(times) // 2], threads
+
+    def single_thread_s(self, op: str, h: dict, rows: int, cols: int) -> float:
+        """Seconds for the whole matrix on one thread, from a row sample of
+        about 2M elements, repeated to at least 30 ms."""
+        fn = self._fn(op, h)
+        k = max(1, min(rows, -(-(1 << 21) // cols)))
+        times, total = [], 0.0
+        while not times or (total < 0.03 and len(times) < 100):
+            t0 = time.perf_counter()
+            fn(0, k)
+            dt = time.perf_counter() - t0
+            times.append(dt)
+            total += dt
+        times.sort()
+        return times[len(times) // 2] * rows / k
+
+    def check(self, got: dict, ref: dict, bf16: bool) -> dict:
+        """Every element: float outputs within 1e-5 + 1e-5 |ref|, bfloat16
+        outputs within one bfloat16 ulp of the oracle + 1e-5; NaN where the
+        oracle has NaN. Returns the element count and the worst err/bound."""
+        import numpy as np
+        o = self.oracle
+        n, worst, bad = 0, 0.0, 0
+        for k, r in ref.items():
+            g = got[k]
+            if g.shape != r.shape:
+                return {"elements": 0, "ok": False, "error": f"{k}: shape {g.shape} vs {r.shape}"}
+            gf, rf = g.reshape(-1), r.reshape(-1)
+            step = 1 << 24
+            for s in range(0, rf.size, step):
+                if bf16 and k == "y":
+                    gv = o.bf16_to_float(gf[s:s + step]).astype(np.float64)
+                    rv = o.bf16_to_float(rf[s:s + step]).astype(np.float64)
+                    e = np.floor(np.log2(np.maximum(np.abs(rv), 2.0 ** -133)))
+                    bound = np.maximum(2.0 ** (e - 7), 2.0 ** -133) + 1e-5
+                else:
+                    gv = gf[s:s + step].astype(np.float64)
+                    rv = rf[s:s + step].astype(np.float64)
+                    bound = 1e-5 + 1e-5 * np.abs(rv)
+                nan_r = np.isnan(rv)
+                bad += int(np.count_nonzero(np.isnan(gv) != nan_r))
+                ratio = np.where(nan_r, 0.0, np.abs(gv - rv) / bound)
+                ratio = np.where(np.isnan(ratio), np.inf, ratio)
+                bad += int(np.count_nonzero(ratio > 1.0))
+                worst = max(worst, float(ratio.max(initial=0.0)))
+                n += rf[s:s + step].size
+        return {"elements": n, "max_err_over_bound": round(worst, 4), "ok": bad == 0}
+
+    def timed_reference(self, op: str, h: dict, rows: int, cols: int, nbytes: int):
+        """The oracle's outputs for the whole matrix, and its timings (all
+        threads, and one thread) in the bench row's units."""
+        ref, secs, threads = self.reference(op, h, rows)
+        one = self.single_thread_s(op, h, rows, cols)
+        # The baseline is the faster of the two (a thread pool costs more
+        # than a tiny matrix takes on one thread).
+        best_s, best_t = (secs, threads) if secs <= one else (one, 1)
+        us = best_s * 1e6
+        return ref, {"us_per_op": round(us, 2), "threads": best_t,
+                     "us_per_op_all_threads": round(secs * 1e6, 2), "all_threads": threads,
+                     "us_per_op_1thread": round(one * 1e6, 2),
+                     "rows_per_s": round(rows / best_s, 1), "GBps": round(nbytes / (us * 1e3), 3)}
+
+    def row(self, op: str, h: dict, rows: int, cols: int, got: dict, nbytes: int, gpu_us: float) -> dict:
+        """Full check of `got` and the oracle's timings for one bench row."""
+        ref, timing = self.timed_reference(op, h, rows, cols, nbytes)
+        parity = self.check(got, ref, op.endswith("_bf16"))
+        del ref
+        return {"parity": parity,
+                "oracle": dict(timing, gpu_speedup=round(timing["us_per_op"] / gpu_us, 1) if gpu_us else None)}
+
+    def headline(self, x_np, w_np, eps, budget_s: float) -> dict:
+        """The bounded CPU baseline of the headline: row blocks of the 16384 x
+        8192 input, first on one thread, then on `cores` threads with a static
+        row split (the oracle's C call releases the GIL), each leg for about
+        half the time budget."""
+        import concurrent.futures as cf
+        rows, cols = x_np.shape
+        block = 256
+
+        def leg(threads: int, seconds: float):
+            t0 = time.perf_counter()
+            done = 0
+            r = 0
+            with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+                while time.perf_counter() - t0 < seconds:
+                    starts = [(r + i * block) % rows for i in range(threads)]
+                    list(ex.map(lambda s0: self.oracle.rmsnorm(x_np[s0:s0 + block], w_np, eps), starts))
+                    done += threads * block
+                    r = (r + threads * block) % rows
+            return done, time.perf_counter() - t0
+
+        d1, t1 = leg(1, budget_s * 0.4)
+        dn, tn = leg(self.cores, budget_s * 0.6)
+        gbps = lambda d, t: (8 * d * cols + 4 * cols) / t / 1e9
+        return {"value": round(gbps(dn, tn), 3), "unit": "GB/s", "cores": self.cores, "kind": "oracle",
+                "us_per_op": round(tn / dn * rows * 1e6, 1), "rows_per_s": round(dn / tn, 1),
+                "single_thread_GBps": round(gbps(d1, t1), 3),
+                "sample": f"rmsnorm 16384x8192 rows in 256-row blocks: {dn} rows on {self.cores} "
+                          f"threads in {tn:.1f} s, {d1} on 1 in {t1:.1f} s"}
+
+
+# ---- GPU tables ---------------------------------------------------------------
+
+def gpu_output(torch, case) -> dict:
+    """Set 0's output after the last launch, as numpy (bfloat16 as bits)."""
+    import numpy as np
+    out = case.output()
+    base = case.base
+    key = "out" if base in ("sum", "cross_entropy") else "y"
+    if out.dtype == torch.bfloat16:
+        return {key: out.view(torch.int16).cpu().numpy().view(np.uint16)}
+    return {key: out.cpu().numpy()}
+
+
+def time_case(torch, case, plan, samples: int) -> dict:
+    from row_reduction_amd.tune import GraphTimer, launches_per_graph
+    n = launches_per_graph(torch, case, plan)
+    gt = GraphTimer(torch, case, plan, n)
+    vals = [gt.sample_us() for _ in range(samples)]
+    s = sorted(vals)
+    del gt
+    return {"us": s[len(s) // 2], "min_us": s[0], "max_us": s[-1], "launches_per_graph": n,
+            "samples_us": [round(v, 4) for v in vals]}
+
+
+def plan_str(plan) -> str:
+    from row_reduction_amd.plans import plan_key
+    return plan_key(plan)
+
+
+def shape_table(torch, rr, workloads, device, ceilings, leg, src_hash, samples: int = 15) -> list:
+    """Every measured (operator, shape) with the selected plan, hot and (for
+    working sets of 1 MiB or more) cold, each row checked in full against the
+    oracle before it is timed."""
+    from row_reduction_amd.tune import Case
+    out = []
+    pairs = [("rmsnorm", s) for s in [(1, 127), (17, 257), (64, 4096), (1024, 4096)]]
+    pairs += [(op, s) for s in workloads.FAMILY_SHAPES for op in workloads.OPS if op != "rmsnorm"]
+    pairs += [("rmsnorm_bf16", s) for s in [(1, 127), (17, 257), (64, 4096), (1024, 4096), (16384, 8192)]]
+    pairs += [(op + "_bf16", s) for s in workloads.FAMILY_SHAPES for op in workloads.OPS if op != "rmsnorm"]
+    for op, (rows, cols) in pairs:
+        plan = rr.rr_select_plan(op, rows, cols)
+        nbytes = workloads.algorithmic_bytes(op, rows, cols)
+        base = op[:-5] if op.endswith("_bf16") else op
+        ref = timing = None
+        inherently_cold = False
+        for hot in (True, False):
+            if not hot and inherently_cold:
+                break
+            case = Case(torch, op, rows, cols, False, device, hot=hot)
+            if not hot and not case.cold_possible:
+                continue
+            inherently_cold = hot and case.cold
+            # The output of this row's own buffers, checked before timing.
+            case.launch(0, plan)
+            torch.cuda.synchronize()
+            parity = None
+            if leg is not None:
+                if ref is None:
+                    ref, timing = leg.timed_reference(op, case.host, rows, cols, nbytes)
+                parity = leg.check(gpu_output(torch, case), ref, op.endswith("_bf16"))
+            t = time_case(torch, case, plan, samples)
+            single = []
+            if hot:
+                for _ in range(21):
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    case.launch(0, plan)
+                    torch.cuda.synchronize()
+                    single.append((time.perf_counter() - t0) * 1e6)
+                single.sort()
+            us = t["us"]
+            gbps = nbytes / (us * 1e3)
+            ceil = ceilings.get(nbytes, base in ("sum", "cross_entropy"), case.cold)
+            row = {"op": op, "shape": f"{rows}x{cols}", "cache": "cold" if case.cold else "hot",
+                   "us_per_op": round(us, 3), "min_us": round(t["min_us"], 3), "max_us": round(t["max_us"], 3),
+                   "launches_per_graph": t["launches_per_graph"], "samples_us": t["samples_us"],
+                   "rows_per_s": round(rows / (us * 1e-6), 1), "GBps": round(gbps, 1),
+                   "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                   "single_call_us": round(single[len(single) // 2], 2) if single else None,
+                   "stream_ceiling": ceil, "frac_of_ceiling": round(ceil["us"] / us, 3),
+                   "plan": plan_str(plan), "source_sha256": src_hash[:16]}
+            if parity is not None:
+                row["parity"] = parity
+                row["oracle"] = dict(timing, gpu_speedup=round(timing["us_per_op"] / us, 1))
+            out.append(row)
+            del case
+            torch.cuda.empty_cache()
+    return out
+
+
+def long_rows_table(torch, rr, device, leg, src_hash, samples: int = 11) -> list:
     """Few long rows: the plan the plain entry points use (one workgroup per
     row, register or streaming path) against the split-row plan the *_ws
-    entry points select with a workspace, per call (graph-replayed), hot and
-    cycling distinct buffers."""
+    entry points select with a workspace, per call (graph-replayed), cycling
+    distinct buffers; both outputs checked in full against the oracle."""
     from row_reduction_amd import workloads
-    from row_reduction_amd.tune import Case, GraphTimer, launches_per_graph
+    from row_reduction_amd.tune import Case
     out = []
     shapes = [(1, 1 << 20), (8, 1 << 18), (32, 65536)]
     for op in ("rmsnorm", "softmax", "row_sum", "rmsnorm_bf16"):
         opn = "sum" if op == "row_sum" else op
         for rows, cols in shapes:
-            rec = {"op": opn, "shape": f"{rows}x{cols}"}
+            rec = {"op": opn, "shape": f"{rows}x{cols}", "source_sha256": src_hash[:16]}
             for mode, ws in (("plain", False), ("split", True)):
                 case = Case(torch, opn, rows, cols, False, device, hot=False, workspace=ws)
-                plan = None
-                n = launches_per_graph(torch, case, plan)
-                gt = GraphTimer(torch, case, plan, n)
-                vals = sorted(gt.sample_us() for _ in range(samples))
-                us = vals[len(vals) // 2]
+                case.launch(0, None)
+                torch.cuda.synchronize()
+                got = gpu_output(torch, case) if leg is not None else None
+                t = time_case(torch, case, None, samples)
+                us = t["us"]
                 nbytes = workloads.algorithmic_bytes(opn, rows, cols)
-                chosen = rr.rr_select_plan(opn, rows, cols).as_dict() if not ws else None
                 rec[mode] = {"us_per_op": round(us, 3), "GBps": round(nbytes / (us * 1e3), 1),
-                             "cache": "cold" if case.cold else "hot",
-                             "plan": chosen if chosen else "split (selected with workspace)"}
-                del gt, case
+                             "samples_us": t["samples_us"], "cache": "cold" if case.cold else "hot",
+                             "plan": plan_str(rr.rr_select_plan(opn, rows, cols)) if not ws
+                             else "split (selected with workspace)"}
+                if got is not None:
+                    chk = leg.row(opn, case.host, rows, cols, got, nbytes, us)
+                    rec[mode]["parity"] = chk["parity"]
+                    if mode == "plain":
+                        rec["oracle"] = chk["oracle"]
+                del case
                 torch.cuda.empty_cache()
             rec["split_speedup"] = round(rec["plain"]["us_per_op"] / rec["split"]["us_per_op"], 3)
             out.append(rec)
     return out
 
 
-def streaming_table(torch, rr, device, samples: int = 9) -> list:
+def streaming_table(torch, rr, device, ceilings, leg, src_hash, samples: int = 9) -> list:
     """Rows beyond the register path (vocabulary-size cross-entropy and
     softmax, 65536-column normalisations), many of them: the streaming plan
     the selector picks, per call (graph-replayed; every input here is larger
-    than the last-level cache), next to a same-bytes copy."""
+    than the last-level cache), next to the same-bytes stream ceiling; each
+    checked in full against the oracle."""
     from row_reduction_amd import workloads
-    from row_reduction_amd.tune import Case, GraphTimer, launches_per_graph
+    from row_reduction_amd.tune import Case
     out = []
     cases = [("cross_entropy", 2048, 128256), ("cross_entropy_bf16", 2048, 128256),
              ("softmax", 2048, 128256), ("softmax_bf16", 2048, 128256),
@@ -260,17 +499,25 @@ def streaming_table(torch, rr, device, samples: int = 9) -> list:
     for op, rows, cols in cases:
         case = Case(torch, op, rows, cols, False, device)
         plan = rr.rr_select_plan(op, rows, cols)
-        n = launches_per_graph(torch, case, plan)
-        gt = GraphTimer(torch, case, plan, n)
-        vals = sorted(gt.sample_us() for _ in range(samples))
-        us = vals[len(vals) // 2]
-        del gt, case
-        torch.cuda.empty_cache()
+        case.launch(0, plan)
+        torch.cuda.synchronize()
+        got = gpu_output(torch, case) if leg is not None else None
+        t = time_case(torch, case, plan, samples)
+        us = t["us"]
         nbytes = workloads.algorithmic_bytes(op, rows, cols)
-        out.append({"op": op, "shape": f"{rows}x{cols}", "us_per_op": round(us, 3),
-                    "GBps": round(nbytes / (us * 1e3), 1),
-                    "frac_of_peak": round(nbytes / (us * 1e3) / PEAK_HBM_GBPS, 4),
-                    "plan": plan.as_dict()})
+        base = op[:-5] if op.endswith("_bf16") else op
+        row = {"op": op, "shape": f"{rows}x{cols}", "us_per_op": round(us, 3), "samples_us": t["samples_us"],
+               "GBps": round(nbytes / (us * 1e3), 1), "frac_of_peak": round(nbytes / (us * 1e3) / PEAK_HBM_GBPS, 4),
+               "plan": plan_str(plan), "source_sha256": src_hash[:16]}
+        host = case.host
+        del case
+        torch.cuda.empty_cache()
+        ceil = ceilings.get(nbytes, base in ("sum", "cross_entropy"), True)
+        row["stream_ceiling"] = ceil
+        row["frac_of_ceiling"] = round(ceil["us"] / us, 3)
+        if got is not None:
+            row.update(leg.row(op, host, rows, cols, got, nbytes, us))
+        out.append(row)
     return out
 
 
@@ -412,56 +659,17 @@ def single_call_table(torch, rr, device, reps: int = 200) -> dict:
     return res
 
 
-def cpu_baseline(workloads, x_np, w_np, eps, y_gpu_sample, budget_s: float = 10.0) -> dict:
-    """The CPU oracle, as it is (plain fp64 C loops), on row blocks of the
-    headline input: first on one thread, then on every host core with a
-    static row split (the oracle's C call releases the GIL), each leg for
-    about half the time budget. Also checks the GPU output on the first block."""
-    import concurrent.futures as cf
-
-    import numpy as np
-
-    import oracle
-    rows, cols = x_np.shape
-    block = 256
-    first = oracle.rmsnorm(x_np[:block], w_np, eps)
-
-    def leg(threads: int, seconds: float):
-        t0 = time.perf_counter()
-        done = 0
-        r = 0
-        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
-            while time.perf_counter() - t0 < seconds:
-                starts = [(r + i * block) % rows for i in range(threads)]
-                list(ex.map(lambda s0: oracle.rmsnorm(x_np[s0:s0 + block], w_np, eps), starts))
-                done += threads * block
-                r = (r + threads * block) % rows
-        return done, time.perf_counter() - t0
-
-    cores = host_cores()
-    d1, t1 = leg(1, budget_s * 0.4)
-    dn, tn = leg(cores, budget_s * 0.6)
-    gbps = lambda d, t: (8 * d * cols + 4 * cols) / t / 1e9
-    err = np.abs(y_gpu_sample.astype(np.float64) - first.astype(np.float64))
-    ok = bool(np.all(err <= 1e-5 + 1e-5 * np.abs(first.astype(np.float64))))
-    cpu = platform.processor() or ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
-    return {"value": round(gbps(dn, tn), 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "us_per_op_full_shape": round(tn / dn * rows * 1e6, 1),
-            "rows_per_s": round(dn / tn, 1),
-            "single_thread_GBps": round(gbps(d1, t1), 3),
-            "single_thread_rows_per_s": round(d1 / t1, 1),
-            "sample": f"rmsnorm_f32 16384x8192 input in blocks of {block} rows: {dn} rows on "
-                      f"{cores} threads in {tn:.1f} s, {d1} rows on 1 thread in {t1:.1f} s "
-                      "(fp64 C loops, static row split)",
-            "cpu_model": cpu, "gpu_matches_oracle_on_first_block": ok}
+def row_line(r: dict) -> str:
+    """One stderr line per bench row."""
+    par = r.get("parity")
+    p = "parity -" if par is None else (f"parity ok ({par['elements']} el, max {par['max_err_over_bound']})"
+                                        if par["ok"] else "PARITY FAILED")
+    o = r.get("oracle")
+    oc = "" if o is None else f" | oracle {o['us_per_op']} us ({o['threads']} thr), x{o['gpu_speedup']}"
+    c = r.get("stream_ceiling")
+    cc = "" if c is None else f" | ceiling {c['us']} us ({r['frac_of_ceiling']:.2f})"
+    return (f"{r['op']:>24} {r['shape']:>12} {r.get('cache', 'cold'):>4}: {r['us_per_op']:9.3f} us "
+            f"{r['GBps']:8.1f} GB/s{cc}{oc} | {p} | {r['plan']}")
 
 
 def main() -> int:
@@ -469,9 +677,12 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--no-shapes", action="store_true", help="skip the per-shape table")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-shapes", action="store_true", help="skip the per-shape, long-row, streaming "
+                                                             "and single-call tables")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle (baseline and parity checks)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--detail", default=os.path.join("gpurun_out", "bench_detail.json"),
+                    help="where the full result (every table) is written")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -480,7 +691,6 @@ def main() -> int:
               "per-GPU kernel is the one measured here at N=1.", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import row_reduction_amd as rr
@@ -504,7 +714,7 @@ def main() -> int:
     def step():
         rr.rmsnorm_f32(x, w, wl.eps, y=y)
 
-    log(f"warmup {args.warmup} steps, plan {plan.as_dict()}")
+    log(f"warmup {args.warmup} steps, plan {plan_str(plan)}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -521,25 +731,72 @@ def main() -> int:
     value = nbytes * args.steps / wall / 1e9
     avg_kernel_us = kernel_ms * 1e3 / args.steps
     achieved = nbytes / (avg_kernel_us * 1e3)
-    src_hash = kernel_source_hash()
-    traffic = counter_traffic(src_hash)
+    kernel_hash = kernel_source_hash()
+    src_hash = device_source_hash()
+    traffic = counter_traffic(kernel_hash)
 
-    # Same-bytes streaming copy (practical ceiling) and the empty-kernel floor.
-    copy_src = x.view(-1)
-    copy_dst = y.view(-1)
-    copy = batch_us(torch, lambda: rr.rr_copy_f32(copy_src, copy_dst), rounds=1)
+    ceilings = Ceilings(torch, rr, device)
+    head_ceiling = ceilings.get(nbytes, False, True)
     empty = graph_us(torch, lambda: rr.rr_empty_kernel(), 200)
-    copy_gbps = 8 * rows * cols / (copy["us"] * 1e3)
+    log(f"headline {avg_kernel_us:.2f} us/launch = {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBPS:.3f} of peak); "
+        f"fastest same-bytes copy {head_ceiling['us']} us ({head_ceiling['packs_per_thread']} packs x "
+        f"{head_ceiling['block']}); launch floor {empty['us']:.3f} us")
 
-    y_sample = None
-    if not args.no_cpu:
-        step()
-        torch.cuda.synchronize()
-        y_sample = y[:256].cpu().numpy()
-    shapes = [] if args.no_shapes else shape_table(torch, rr, workloads, device)
-    long_rows = [] if args.no_shapes else long_rows_table(torch, rr, device)
-    streaming = [] if args.no_shapes else streaming_table(torch, rr, device)
-    single = {} if args.no_shapes else single_call_table(torch, rr, device)
+    cores, cores_avail = host_cores()
+    leg = None if args.no_cpu else OracleLeg(cores)
+    head_parity = None
+    if leg is not None:
+        log("headline: full oracle check of the output")
+        y_np = y.cpu().numpy()
+        ref, secs, threads = leg.reference("rmsnorm", {"x": wl.x, "w": wl.w, "eps": wl.eps}, rows)
+        head_parity = leg.check({"y": y_np}, ref, False)
+        del ref, y_np
+        log(f"headline parity: {head_parity}")
+
+    shapes = long_rows = streaming = []
+    single = {}
+    if not args.no_shapes:
+        shapes = shape_table(torch, rr, workloads, device, ceilings, leg, src_hash)
+        for r in shapes:
+            log(row_line(r))
+        long_rows = long_rows_table(torch, rr, device, leg, src_hash)
+        for r in long_rows:
+            for mode in ("plain", "split"):
+                p = r[mode].get("parity")
+                log(f"{r['op']:>24} {r['shape']:>12} {mode:>5}: {r[mode]['us_per_op']:9.3f} us "
+                    f"{r[mode]['GBps']:8.1f} GB/s | parity {'-' if p is None else ('ok' if p['ok'] else 'FAILED')}")
+        streaming = streaming_table(torch, rr, device, ceilings, leg, src_hash)
+        for r in streaming:
+            log(row_line(r))
+        single = single_call_table(torch, rr, device)
+        log(f"single call: {single}")
+
+    cpu = None
+    if leg is not None:
+        log(f"cpu baseline ({args.cpu_seconds:.0f} s)")
+        cpu = leg.headline(wl.x, wl.w, wl.eps, args.cpu_seconds)
+        cpu["cores_available"] = cores_avail
+        cpu["cpu_model"] = cpu_model()
+        cpu["gpu_over_oracle"] = round(value / cpu["value"], 1)
+
+    checks = [r.get("parity") for r in shapes + streaming]
+    checks += [r[m].get("parity") for r in long_rows for m in ("plain", "split")]
+    checks = [c for c in checks if c is not None] + ([head_parity] if head_parity else [])
+    failed = sum(1 for c in checks if not c["ok"])
+
+    detail = {
+        "metric": METRIC, "source_sha256": src_hash, "kernel_fingerprint": kernel_hash,
+        "headline": {"us_per_launch": avg_kernel_us, "GBps": achieved, "parity": head_parity,
+                     "plan": plan_str(plan)},
+        "stream_ceiling": head_ceiling, "launch_floor_us": round(empty["us"], 3),
+        "device": device_info(torch), "cpu_baseline": cpu,
+        "shapes": shapes, "long_rows": long_rows, "streaming_rows": streaming, "single_call": single,
+    }
+    if args.detail:
+        os.makedirs(os.path.dirname(os.path.abspath(args.detail)), exist_ok=True)
+        with open(args.detail, "w") as f:
+            json.dump(detail, f)
+        log(f"detail written to {args.detail}")
 
     result = {
         "metric": METRIC,
@@ -556,28 +813,23 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic (seeded numpy: x~N(0,1), w~U(0.5,1.5))",
         "config": {"workload": "rmsnorm_f32 16384x8192, eps=1e-6", "rows": rows, "cols": cols,
-                   "plan": plan.as_dict(), "parallelism": "single GPU"},
+                   "plan": plan_str(plan), "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
-                     "kernel_source_sha256": src_hash},
-        "copy_ceiling": {"bytes": 8 * rows * cols, "us": round(copy["us"], 2),
-                         "GBps": round(copy_gbps, 1), "frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4)},
-        "launch_floor_us": round(empty["us"], 3),
-        "device": device_info(torch),
-        "shapes": shapes,
-        "long_rows": long_rows,
-        "streaming_rows": streaming,
-        "single_call": single,
+                     "kernel_source_sha256": kernel_hash[:16]},
+        "stream_ceiling_us": head_ceiling["us"],
+        "cpu_baseline": None if cpu is None else {
+            k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample", "us_per_op", "rows_per_s",
+                                "cores_available", "cpu_model")},
+        "parity": {"checked": len(checks), "failed": failed,
+                   "headline_max_err_over_bound": head_parity["max_err_over_bound"] if head_parity else None},
+        "detail": args.detail,
     }
-    if not args.no_cpu:
-        log(f"cpu baseline ({args.cpu_seconds:.0f} s)")
-        result["cpu_baseline"] = cpu_baseline(workloads, wl.x, wl.w, wl.eps, y_sample, args.cpu_seconds)
-        result["cpu_baseline"]["gpu_over_oracle"] = round(value / result["cpu_baseline"]["value"], 1)
-    else:
-        result["cpu_baseline"] = None
-    _ = np
-    print(json.dumps(result), flush=True)
+    line = json.dumps(result, ensure_ascii=False)
+    if len(line.encode()) > 2048:
+        raise SystemExit(f"headline JSON line is {len(line.encode())} bytes; keep it under 2 KB")
+    print(line, flush=True)
     return 0
 
 

@@ -396,6 +396,15 @@ const char *rr_status_string(int status);
 /* dst[i] = src[i] for 0 <= i < n (n floats; no overlap). */
 int rr_copy_f32(const float *src, float *dst, int64_t n, void *stream);
 
+/* A streaming kernel of chosen geometry over n floats, for the fastest
+ * stream of a given size: copy != 0 copies src to dst; copy == 0 only reads
+ * src (dst, at least ceil(n / (4 * packs_per_thread * block)) * block
+ * floats, is passed but never written). Each thread moves packs_per_thread
+ * (1, 2, 4 or 8) non-temporal 16-byte packs in groups of `block` (256, 512
+ * or 1024) threads; other geometries return RR_ERR_UNSUPPORTED. */
+int rr_stream_f32(const float *src, float *dst, int64_t n, int32_t copy, int32_t packs_per_thread,
+                  int32_t block, void *stream);
+
 /* Launches one workgroup of one wavefront that does nothing. */
 int rr_empty_kernel(void *stream);
 

@@ -21,7 +21,7 @@ __all__ = [
     "rmsnorm_bf16", "row_sum_bf16", "softmax_bf16", "layernorm_bf16",
     "residual_layernorm_bf16", "cross_entropy_bf16",
     "rr_select_plan", "rr_select_plan_from", "rr_model_time_us", "rr_check_plan", "rr_status_string",
-    "rr_copy_f32", "rr_empty_kernel",
+    "rr_copy_f32", "rr_stream_f32", "rr_empty_kernel",
     "rr_workspace_bytes", "workspace_for", "batch_problem", "rr_batch",
     "rr_plan", "RowRedError", "OP_IDS",
 ]
@@ -381,6 +381,24 @@ def rr_copy_f32(src, dst, stream=None):
         raise ValueError("src and dst sizes differ")
     _capi.check("rr_copy_f32", _capi.lib().rr_copy_f32(src.data_ptr(), dst.data_ptr(), src.numel(),
                                                         _stream(stream)))
+    return dst
+
+
+def rr_stream_f32(src, dst, copy=True, packs_per_thread=1, block=256, stream=None):
+    """Streaming kernel of a chosen geometry over src (float32): copy into dst,
+    or (copy=False) read only, dst being passed but never written. dst needs
+    src's size for a copy, else at least one float per thread launched."""
+    torch = _torch()
+    for t, n in ((src, "src"), (dst, "dst")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda \
+                or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous float32 CUDA/HIP tensor")
+    n = src.numel()
+    need = n if copy else -(-n // (4 * packs_per_thread * block)) * block
+    if dst.numel() < need:
+        raise ValueError(f"dst holds {dst.numel()} floats, {need} needed")
+    _capi.check("rr_stream_f32", _capi.lib().rr_stream_f32(src.data_ptr(), dst.data_ptr(), n, int(bool(copy)),
+                                                            packs_per_thread, block, _stream(stream)))
     return dst
 
 

@@ -58,7 +58,7 @@ EXPORTED = (
     "rr_workspace_bytes",
     "rr_select_plan", "rr_check_plan", "rr_status_string",
     "rr_select_plan_from", "rr_model_time_us", "rr_batch",
-    "rr_copy_f32", "rr_empty_kernel",
+    "rr_copy_f32", "rr_stream_f32", "rr_empty_kernel",
 )
 
 # rr_plan_source
@@ -159,6 +159,7 @@ _SIGNATURES = {
     "rr_batch": [ctypes.POINTER(rr_problem), ctypes.c_int32, _vp],
     "rr_status_string": [ctypes.c_int],
     "rr_copy_f32": [_vp, _vp, _i64, _vp],
+    "rr_stream_f32": [_vp, _vp, _i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp],
     "rr_empty_kernel": [_vp],
 }
 

@@ -40,6 +40,79 @@ __global__ void __launch_bounds__(kCopyBlock) copy_kernel(const float *__restric
 
 __global__ void __launch_bounds__(64) empty_kernel() {}
 
+// Streaming kernel of a chosen geometry, for a ceiling at any size: each
+// thread moves PACKS non-temporal float4 packs, pack (g * PACKS + u) * BLOCK
+// + t for thread t of group g; group 0 also takes the n % 4 trailing floats.
+// COPY: dst = src. Read-only: every pack is loaded and summed, and the sum is
+// stored only if it equals `sentinel`, which the host passes as NaN (no float
+// equals it), so nothing is written but no load can be dropped.
+template <int PACKS, int BLOCK, bool COPY>
+__global__ void __launch_bounds__(BLOCK) stream_kernel(const float *__restrict__ src, float *__restrict__ dst,
+                                                       int64_t n, float sentinel) {
+    const int64_t packs = n / 4;
+    const int64_t first = (int64_t)blockIdx.x * PACKS * BLOCK + threadIdx.x;
+    const f32x4u *s4 = reinterpret_cast<const f32x4u *>(src) + first;
+    f32x4u *d4 = reinterpret_cast<f32x4u *>(dst) + first;
+    float acc = 0.0f;
+    if (first + (int64_t)(PACKS - 1) * BLOCK < packs) {
+        // Every pack of this thread exists: all loads issued, then all stores.
+        f32x4u v[PACKS];
+#pragma unroll
+        for (int u = 0; u < PACKS; ++u) v[u] = __builtin_nontemporal_load(s4 + u * BLOCK);
+#pragma unroll
+        for (int u = 0; u < PACKS; ++u) {
+            if constexpr (COPY) __builtin_nontemporal_store(v[u], d4 + u * BLOCK);
+            else acc += (v[u].x + v[u].y) + (v[u].z + v[u].w);
+        }
+    } else {
+        // The last group's threads: one pack at a time, each guarded.
+        for (int u = 0; u < PACKS && first + (int64_t)u * BLOCK < packs; ++u) {
+            const f32x4u t = __builtin_nontemporal_load(s4 + u * BLOCK);
+            if constexpr (COPY) __builtin_nontemporal_store(t, d4 + u * BLOCK);
+            else acc += (t.x + t.y) + (t.z + t.w);
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
+        if constexpr (COPY) dst[4 * packs + threadIdx.x] = src[4 * packs + threadIdx.x];
+        else acc += src[4 * packs + threadIdx.x];
+    }
+    if constexpr (!COPY) {
+        if (acc == sentinel) dst[(int64_t)blockIdx.x * BLOCK + threadIdx.x] = acc;
+    }
+}
+
+template <int PACKS, int BLOCK, bool COPY>
+void launch_stream(const float *src, float *dst, int64_t n, int64_t groups, hipStream_t s) {
+    hipLaunchKernelGGL((stream_kernel<PACKS, BLOCK, COPY>), dim3((unsigned)groups), dim3(BLOCK), 0, s, src, dst,
+                       n, __builtin_nanf(""));
+}
+
+template <int PACKS, bool COPY>
+int stream_by_block(int block, const float *src, float *dst, int64_t n, hipStream_t s) {
+    const int64_t per_group = (int64_t)PACKS * block;
+    int64_t groups = (n / 4 + per_group - 1) / per_group;
+    if (groups == 0) groups = 1;
+    if (groups > 0x7fffffff) return RR_ERR_UNSUPPORTED;
+    switch (block) {
+        case 256: launch_stream<PACKS, 256, COPY>(src, dst, n, groups, s); break;
+        case 512: launch_stream<PACKS, 512, COPY>(src, dst, n, groups, s); break;
+        case 1024: launch_stream<PACKS, 1024, COPY>(src, dst, n, groups, s); break;
+        default: return RR_ERR_UNSUPPORTED;
+    }
+    return hipGetLastError() == hipSuccess ? RR_OK : RR_ERR_LAUNCH;
+}
+
+template <bool COPY>
+int stream_by_packs(int packs, int block, const float *src, float *dst, int64_t n, hipStream_t s) {
+    switch (packs) {
+        case 1: return stream_by_block<1, COPY>(block, src, dst, n, s);
+        case 2: return stream_by_block<2, COPY>(block, src, dst, n, s);
+        case 4: return stream_by_block<4, COPY>(block, src, dst, n, s);
+        case 8: return stream_by_block<8, COPY>(block, src, dst, n, s);
+        default: return RR_ERR_UNSUPPORTED;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -57,6 +130,17 @@ int rr_copy_f32(const float *src, float *dst, int64_t n, void *stream) {
     hipLaunchKernelGGL(copy_kernel, dim3((unsigned)groups), dim3(kCopyBlock), 0,
                        reinterpret_cast<hipStream_t>(stream), src, dst, n);
     return hipGetLastError() == hipSuccess ? RR_OK : RR_ERR_LAUNCH;
+}
+
+int rr_stream_f32(const float *src, float *dst, int64_t n, int32_t copy, int32_t packs_per_thread,
+                  int32_t block, void *stream) {
+    if (n < 0) return RR_ERR_INVALID_ARGUMENT;
+    if (n == 0) return RR_OK;
+    const uintptr_t bits = reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst);
+    if (src == nullptr || dst == nullptr || (bits & 3u)) return RR_ERR_INVALID_ARGUMENT;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return copy ? stream_by_packs<true>(packs_per_thread, block, src, dst, n, s)
+                : stream_by_packs<false>(packs_per_thread, block, src, dst, n, s);
 }
 
 int rr_empty_kernel(void *stream) {

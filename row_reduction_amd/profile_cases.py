@@ -9,6 +9,13 @@ writes a manifest of what it launched, in order. Run it under
   rocprofv3 --kernel-trace --output-format csv -d OUT -o cases -- \\
       python3 <repo>/row_reduction_amd/profile_cases.py run --manifest OUT/manifest.json
 
+Options: `--isolated` issues each measured launch as its own synchronised
+call (the kernel starts on an idle GPU; nothing overlaps its start or its
+drain); `--all-plans` runs every legal plan of each case, not only the
+selected one; `--ceilings` adds rr_stream_f32 in every geometry moving each
+case's algorithmic bytes (a copy, or a read-only stream for row sum and
+cross-entropy), rotated over buffers the same way.
+
 `summarize` then walks the trace's dispatches of librowred kernels in
 dispatch order, attributes them to the manifest's cases (checking each
 dispatch's grid size against the case's), and prints a markdown table of
@@ -57,7 +64,7 @@ def headline_fingerprint() -> str:
     return kernel_fingerprint(rr.rr_select_plan("rmsnorm", 16384, 8192).as_dict())
 
 
-def cases_list(shapes_only=None):
+def cases_list(shapes_only=None, ops_only=None):
     from row_reduction_amd import workloads
     cases = [("rmsnorm", s) for s in [(1, 127), (17, 257), (64, 4096), (1024, 4096), (16384, 8192)]]
     cases += [(op, s) for s in workloads.FAMILY_SHAPES for op in workloads.OPS if op != "rmsnorm"]
@@ -69,6 +76,8 @@ def cases_list(shapes_only=None):
               ("rmsnorm", (4096, 65536)), ("layernorm", (4096, 65536))]
     if shapes_only:
         cases = [c for c in cases if f"{c[1][0]}x{c[1][1]}" in shapes_only]
+    if ops_only:
+        cases = [c for c in cases if c[0] in ops_only]
     return cases
 
 
@@ -76,12 +85,14 @@ def run(args) -> int:
     import torch
 
     import row_reduction_amd as rr
+    from row_reduction_amd import plans as plans_mod
     from row_reduction_amd import workloads
-    from row_reduction_amd.tune import Case
+    from row_reduction_amd.tune import COLD_BYTES, Case
 
     rr._capi.lib()
     device = torch.device("cuda:0")
-    manifest = {"launches": args.launches, "warmup": args.warmup, "entries": []}
+    manifest = {"launches": args.launches, "warmup": args.warmup, "isolated": bool(args.isolated),
+                "entries": []}
 
     def add(name, kind, count, grid, nbytes, warm, extra=None):
         e = {"name": name, "kind": kind, "count": count, "grid_size": grid, "bytes": nbytes,
@@ -90,10 +101,62 @@ def run(args) -> int:
             e.update(extra)
         manifest["entries"].append(e)
 
-    for op, (rows, cols) in cases_list(args.shapes):
-        plan = rr.rr_select_plan(op, rows, cols)
-        groups = -(-rows // plan.rows_per_group)
-        grid = groups * plan.block
+    def measured(launch, first):
+        """The measured launches: back to back from one HIP graph, or (isolated)
+        one launch per synchronised call, so each kernel starts on an idle GPU
+        and nothing overlaps its start or its drain."""
+        if args.isolated:
+            for i in range(args.launches):
+                launch(first + i)
+                torch.cuda.synchronize()
+            return
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.launches):
+                launch(first + i)
+        graph.replay()
+        torch.cuda.synchronize()
+        del graph
+
+    ceilings_done = set()
+
+    def ceilings(nbytes, read_only, cold):
+        """rr_stream_f32 of every geometry moving `nbytes` (a copy: half read,
+        half written; read-only: all read), rotated over distinct buffers like
+        the cold cases."""
+        n = max(4, nbytes // (4 if read_only else 8))
+        key = (n, read_only, cold)
+        if key in ceilings_done:
+            return
+        ceilings_done.add(key)
+        per_set = 4 * n * (1 if read_only else 2)
+        nsets = max(1, min(1024, -(-COLD_BYTES // per_set))) if cold else 1
+        src = [torch.zeros(n, device=device) for _ in range(nsets)]
+        dst = [torch.empty(n, device=device) for _ in range(nsets)]
+        for packs in (1, 2, 4, 8):
+            for block in (256, 512, 1024):
+                groups = max(1, -(-(n // 4) // (packs * block)))
+                label = (f"stream {'read' if read_only else 'copy'} {4 * n * (1 if read_only else 2)} B "
+                         f"{'cold' if cold else 'hot'} packs{packs} b{block}")
+
+                def launch(i, packs=packs, block=block):
+                    k = i % nsets
+                    rr.rr_stream_f32(src[k], dst[k], copy=not read_only, packs_per_thread=packs, block=block)
+                warm = max(args.warmup, nsets)
+                for i in range(warm):
+                    launch(i)
+                add(label, "stream", warm, groups * block, 4 * n * (1 if read_only else 2), True)
+                torch.cuda.synchronize()
+                measured(launch, warm)
+                add(label, "stream", args.launches, groups * block, 4 * n * (1 if read_only else 2), False)
+        del src, dst
+        torch.cuda.empty_cache()
+
+    for op, (rows, cols) in cases_list(args.shapes, args.ops):
+        selected = rr.rr_select_plan(op, rows, cols)
+        plan_list = [selected]
+        if args.all_plans:
+            plan_list = plans_mod.candidate_plans(op, rows, cols, caches=(0, 1, 2))
         nbytes = workloads.algorithmic_bytes(op, rows, cols)
         inherently_cold = False
         for hot in (True, False):
@@ -103,46 +166,44 @@ def run(args) -> int:
             if not hot and not case.cold_possible:
                 continue
             inherently_cold = hot and case.cold
-            label = f"{op} {rows}x{cols} {'cold' if case.cold else 'hot'}"
-            print(f"case {label} plan {plan.as_dict()}", flush=True)
-            # Measured launches run back to back from a HIP graph: a kernel
-            # dispatched onto an idle GPU reports a longer duration.
-            n_warm = max(args.warmup, case.nsets)
-            for i in range(n_warm):
-                case.launch(i, plan)
-            add(label, "op", n_warm, grid, nbytes, True)
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                for i in range(args.launches):
-                    case.launch(n_warm + i, plan)
-            graph.replay()
-            add(label, "op", args.launches, grid, nbytes, False, {"plan": plan.as_dict()})
-            torch.cuda.synchronize()
-            del graph
+            if hot and args.cold_only and case.cold_possible and not case.cold:
+                del case
+                continue
+            for plan in plan_list:
+                groups = -(-rows // plan.rows_per_group)
+                grid = groups * plan.block
+                tag = "" if not args.all_plans else " " + plans_mod.plan_key(plan) + \
+                    (" (selected)" if plan.as_dict() == selected.as_dict() else "")
+                label = f"{op} {rows}x{cols} {'cold' if case.cold else 'hot'}{tag}"
+                print(f"case {label} plan {plan.as_dict()}", flush=True)
+                n_warm = max(args.warmup, case.nsets)
+                for i in range(n_warm):
+                    case.launch(i, plan)
+                add(label, "op", n_warm, grid, nbytes, True)
+                torch.cuda.synchronize()
+                measured(lambda i, plan=plan: case.launch(i, plan), n_warm)
+                add(label, "op", args.launches, grid, nbytes, False, {"plan": plan.as_dict()})
+            if args.ceilings:
+                base = op[:-5] if op.endswith("_bf16") else op
+                ceilings(nbytes, base in ("sum", "cross_entropy"), case.cold)
             del case
             torch.cuda.empty_cache()
 
-    # Same-bytes streaming copy (1 GiB moved) and the empty kernel.
-    n = 16384 * 8192
-    src = torch.zeros(n, dtype=torch.float32, device=device)
-    dst = torch.empty_like(src)
-    copy_grid = -(-(n // 4) // 256) * 256   # one float4 per thread, 256-thread groups
-    for name, kind, fn, grid, nbytes in (
-            ("rr_copy_f32 2^27 floats", "copy", lambda: rr.rr_copy_f32(src, dst), copy_grid, 8 * n),
-            ("rr_empty_kernel", "empty", lambda: rr.rr_empty_kernel(), 64, 0)):
-        for _ in range(args.warmup):
-            fn()
-        add(name, kind, args.warmup, grid, nbytes, True)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(args.launches):
-                fn()
-        graph.replay()
-        add(name, kind, args.launches, grid, nbytes, False)
-        torch.cuda.synchronize()
-        del graph
+    if not args.no_reference:
+        # Same-bytes streaming copy (1 GiB moved) and the empty kernel.
+        n = 16384 * 8192
+        src = torch.zeros(n, dtype=torch.float32, device=device)
+        dst = torch.empty_like(src)
+        copy_grid = -(-(n // 4) // 256) * 256   # one float4 per thread, 256-thread groups
+        for name, kind, fn, grid, nbytes in (
+                ("rr_copy_f32 2^27 floats", "copy", lambda i: rr.rr_copy_f32(src, dst), copy_grid, 8 * n),
+                ("rr_empty_kernel", "empty", lambda i: rr.rr_empty_kernel(), 64, 0)):
+            for i in range(args.warmup):
+                fn(i)
+            add(name, kind, args.warmup, grid, nbytes, True)
+            torch.cuda.synchronize()
+            measured(fn, 0)
+            add(name, kind, args.launches, grid, nbytes, False)
     os.makedirs(os.path.dirname(os.path.abspath(args.manifest)), exist_ok=True)
     with open(args.manifest, "w") as f:
         json.dump(manifest, f)
@@ -153,7 +214,7 @@ def run(args) -> int:
 def ours(name: str) -> bool:
     # The profiler leaves some names mangled (e.g. instances over __bf16).
     return ("rowred::" in name or name.startswith("_ZN6rowred") or "copy_kernel" in name
-            or "empty_kernel" in name)
+            or "empty_kernel" in name or "stream_kernel" in name)
 
 
 def demangle(name: str) -> str:
@@ -264,6 +325,14 @@ def main() -> int:
     r.add_argument("--launches", type=int, default=50)
     r.add_argument("--warmup", type=int, default=5)
     r.add_argument("--shapes", default=None, help="comma-separated subset, e.g. 1024x4096")
+    r.add_argument("--ops", default=None, help="comma-separated subset, e.g. rmsnorm,cross_entropy_bf16")
+    r.add_argument("--isolated", action="store_true",
+                   help="one measured launch per synchronised call instead of a graph of back-to-back launches")
+    r.add_argument("--all-plans", action="store_true", help="every legal plan (all cache policies), not only the selected one")
+    r.add_argument("--ceilings", action="store_true",
+                   help="also every rr_stream_f32 geometry moving each case's bytes")
+    r.add_argument("--cold-only", action="store_true", help="skip the cache-hot runs of cases that can be cold")
+    r.add_argument("--no-reference", action="store_true", help="skip the 1 GiB copy and the empty kernel")
     s = sub.add_parser("summarize")
     s.add_argument("manifest")
     s.add_argument("trace")
@@ -276,6 +345,8 @@ def main() -> int:
     if args.cmd == "run":
         if args.shapes:
             args.shapes = set(args.shapes.split(","))
+        if args.ops:
+            args.ops = set(args.ops.split(","))
         return run(args)
     return summarize(args)
 

@@ -100,6 +100,7 @@ class Case:
         import row_reduction_amd as rr
         self.torch, self.rr, self.op, self.rows, self.cols = torch, rr, op, rows, cols
         h = host_inputs(op, rows, cols, held_out)
+        self.host = h  # the seeded host arrays every buffer set is a copy of
         self.eps = h["eps"]
         self.bf16 = op.endswith("_bf16")
         self.base = op[:-5] if self.bf16 else op

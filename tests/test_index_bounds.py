@@ -221,3 +221,35 @@ def test_widest_rows_keep_every_index_in_32_bits():
                     assert biggest < 2 ** 31, (op, plans.plan_key(p), biggest)
                     n += 1
     assert n > 20
+
+
+def stream_kernel_accesses(n, packs_per_thread, block):
+    """Host model of rr_stream_f32's indexing: (grid, packs read per thread,
+    tail floats) exactly as the kernel forms them."""
+    packs = n // 4
+    groups = max(1, -(-packs // (packs_per_thread * block)))
+    touched = []
+    for g in range(groups):
+        for t in range(block):
+            first = g * packs_per_thread * block + t
+            if first + (packs_per_thread - 1) * block < packs:
+                touched += [first + u * block for u in range(packs_per_thread)]
+            else:
+                u = 0
+                while u < packs_per_thread and first + u * block < packs:
+                    touched.append(first + u * block)
+                    u += 1
+    tail = [4 * packs + t for t in range(block) if t < (n & 3)]
+    return groups, touched, tail
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 1023, 4096, 4099, 65536 + 7, 300001])
+@pytest.mark.parametrize("packs_per_thread", [1, 2, 4, 8])
+@pytest.mark.parametrize("block", [256, 512, 1024])
+def test_stream_kernel_covers_every_float_once_in_bounds(n, packs_per_thread, block):
+    groups, touched, tail = stream_kernel_accesses(n, packs_per_thread, block)
+    assert sorted(touched) == list(range(n // 4)), "every whole pack exactly once"
+    assert all(4 * p + 3 < n for p in touched), "no pack past the end"
+    assert tail == list(range(4 * (n // 4), n)), "trailing floats exactly once"
+    # Read-only form: the never-taken sink index stays inside groups * block floats.
+    assert groups * block >= 1
