@@ -61,21 +61,27 @@ int launch(int op, const rr_plan &p, const Args &a, void *stream) {
 // Everything after pointer validation: workspace check, plan (the caller's,
 // checked, or the selector's within max_v and the workspace), launch.
 // max_v bounds the pack width by the pointers' alignment (bfloat16 storage).
-int run(int op, Args a, const rr_plan *plan, void *workspace, int64_t workspace_bytes, int max_v,
-        void *stream) {
-    if (workspace_bytes < 0 || !ok_opt(workspace, 16)) return RR_ERR_INVALID_ARGUMENT;
-    const int64_t avail = workspace != nullptr ? workspace_bytes : 0;
-    rr_plan p;
+// The plan a call runs: the caller's, checked (its pack width within max_v,
+// its workspace within `avail` bytes), or the selector's within both.
+int resolve_plan(int op, const Args &a, const rr_plan *plan, int64_t avail, int max_v, rr_plan *out) {
     if (plan != nullptr) {
         int st = check_plan(op, a.rows, a.cols, plan);
         if (st != RR_OK) return st == RR_ERR_INVALID_ARGUMENT ? RR_ERR_INVALID_ARGUMENT : RR_ERR_UNSUPPORTED;
         if (plan->v > max_v) return RR_ERR_UNSUPPORTED;
         if (plan_workspace_bytes(a.rows, a.cols, plan) > avail) return RR_ERR_UNSUPPORTED;
-        p = *plan;
-    } else {
-        int st = select_plan(op, a.rows, a.cols, &p, max_v, avail);
-        if (st != RR_OK) return st;
+        *out = *plan;
+        return RR_OK;
     }
+    return select_plan(op, a.rows, a.cols, out, max_v, avail);
+}
+
+int run(int op, Args a, const rr_plan *plan, void *workspace, int64_t workspace_bytes, int max_v,
+        void *stream) {
+    if (workspace_bytes < 0 || !ok_opt(workspace, 16)) return RR_ERR_INVALID_ARGUMENT;
+    const int64_t avail = workspace != nullptr ? workspace_bytes : 0;
+    rr_plan p;
+    const int st = resolve_plan(op, a, plan, avail, max_v, &p);
+    if (st != RR_OK) return st;
     a.workspace = workspace;
     return launch(op, p, a, stream) == (int)hipSuccess ? RR_OK : RR_ERR_LAUNCH;
 }
