@@ -38,8 +38,8 @@
  *     RR_ERR_UNSUPPORTED. A launch the HIP runtime refuses returns
  *     RR_ERR_LAUNCH. Nothing is enqueued unless RR_OK is returned.
  *   - All entry points are reentrant and may be called concurrently from
- *     several host threads. The only global state is a small cache of the
- *     plan model's recent choices, guarded by a mutex.
+ *     several host threads. No state is shared between calls: each host
+ *     thread keeps its own small cache of the plan model's recent choices.
  *   - Arithmetic is float32 (row sum: float64 accumulation, see below); the
  *     order of additions inside a row depends on the plan, as the ownership
  *     map permits.
