@@ -174,6 +174,15 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{LIB_PATH} is not built; run "
                 "`python row_reduction_amd/build.py` first")
+        # torch ships its own HIP runtime under the same soname as ROCm's.
+        # Loading torch first makes this library bind to that one runtime, so
+        # the device pointers and stream handles torch hands over are valid
+        # here. Loaded the other way round, the process would hold two HIP
+        # runtimes and every launch on a torch stream would fail.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         for name, argtypes in _SIGNATURES.items():
             fn = getattr(L, name)

@@ -132,7 +132,7 @@ def run(args) -> int:
         per_set = 4 * n * (1 if read_only else 2)
         nsets = max(1, min(1024, -(-COLD_BYTES // per_set))) if cold else 1
         src = [torch.zeros(n, device=device) for _ in range(nsets)]
-        dst = [torch.empty(n, device=device) for _ in range(nsets)]
+        dst = [torch.empty(n + (1024 if read_only else 0), device=device) for _ in range(nsets)]
         for packs in (1, 2, 4, 8):
             for block in (256, 512, 1024):
                 groups = max(1, -(-(n // 4) // (packs * block)))

@@ -139,7 +139,7 @@ IN_PLACE_OPS = ["rmsnorm", "softmax", "layernorm", "residual_layernorm"]
 def run_in_place(op, t, plan, ws, bf16):
     """One call with y aliasing x (residual LayerNorm: h_out in its own buffer)."""
     import torch
-    eps = t["eps"]
+    eps = t.get("eps")
     x = t["x"]
     sfx = "_bf16" if bf16 else "_f32"
     if op == "rmsnorm":
