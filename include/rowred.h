@@ -38,8 +38,10 @@
  *     RR_ERR_UNSUPPORTED. A launch the HIP runtime refuses returns
  *     RR_ERR_LAUNCH. Nothing is enqueued unless RR_OK is returned.
  *   - All entry points are reentrant and may be called concurrently from
- *     several host threads. No state is shared between calls: each host
- *     thread keeps its own small cache of the plan model's recent choices.
+ *     several host threads. No state is shared between calls (each host
+ *     thread keeps its own small cache of the plan model's recent choices),
+ *     except the static device buffer of rmsnorm_f32_noalloc, whose calls
+ *     on one GPU must not overlap.
  *   - Arithmetic is float32 (row sum: float64 accumulation, see below); the
  *     order of additions inside a row depends on the plan, as the ownership
  *     map permits.
@@ -298,6 +300,28 @@ int residual_layernorm_bf16_ws(const uint16_t *x, const uint16_t *residual, cons
 int cross_entropy_bf16_ws(const uint16_t *logits, const int32_t *targets, float *loss,
                           int64_t rows, int64_t cols,
                           const rr_plan *plan, void *workspace, int64_t workspace_bytes, void *stream);
+
+/* ---- split rows without any allocation ---------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, and harnesses that forbid hipMalloc. As
+ * rmsnorm_f32_ws, with the library's own static device buffer of
+ * RR_NOALLOC_SCRATCH_BYTES (1 MiB: 65536 split partials) as the workspace;
+ * the call allocates and frees nothing, directly or through any library.
+ * With plan == NULL the selector may split rows whose partials fit the
+ * buffer (rows * S * 16 bytes), else it picks as rmsnorm_f32 does; an
+ * explicit split plan needing more returns RR_ERR_UNSUPPORTED before
+ * anything is enqueued. Each GPU holds one such buffer, shared by every call
+ * on that GPU, from the first call until the process ends; the address is
+ * looked up once per device on the calling thread's current device, which
+ * must be the device of `stream`. Nothing in it needs clearing (the first
+ * launch of a split plan writes every partial the second one reads), but
+ * calls that overlap on one GPU (other streams, other host threads) race on
+ * it: serialise them, e.g. on one stream. Other arguments, ownership and
+ * errors are as for rmsnorm_f32_ws (RR_ERR_LAUNCH also when the buffer's
+ * device address cannot be obtained). */
+#define RR_NOALLOC_SCRATCH_BYTES ((int64_t)1 << 20)
+int rmsnorm_f32_noalloc(const float *x, const float *w, float *y, int64_t rows, int64_t cols, float eps,
+                        const rr_plan *plan, void *stream);
 
 /* ---- Batched launch -------------------------------------------------------
  * Many small independent problems in one kernel launch, so that a sequence

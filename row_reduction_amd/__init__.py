@@ -17,7 +17,7 @@ from ._capi import OP_IDS, RowRedError, rr_plan
 
 __all__ = [
     "rmsnorm_f32", "row_sum_f32", "softmax_f32", "layernorm_f32",
-    "residual_layernorm_f32", "cross_entropy_f32",
+    "residual_layernorm_f32", "cross_entropy_f32", "rmsnorm_f32_noalloc",
     "rmsnorm_bf16", "row_sum_bf16", "softmax_bf16", "layernorm_bf16",
     "residual_layernorm_bf16", "cross_entropy_bf16",
     "rr_select_plan", "rr_select_plan_from", "rr_model_time_us", "rr_check_plan", "rr_status_string",
@@ -111,6 +111,20 @@ def rmsnorm_f32(x, w, eps=1e-6, y=None, plan=None, workspace=None, stream=None):
     st = _capi.lib().rmsnorm_f32_ws(x.data_ptr(), w.data_ptr(), y.data_ptr(), rows, cols, float(eps),
                                      _plan_ptr(plan), *_ws(workspace), _stream(stream))
     _capi.check("rmsnorm_f32", st)
+    return y
+
+
+def rmsnorm_f32_noalloc(x, w, eps=1e-6, y=None, plan=None, stream=None):
+    """rmsnorm_f32 whose split-row partials use the library's static device
+    buffer (no workspace, nothing allocated by the call when y is given).
+    Calls on one GPU share that buffer: overlapping calls race. Returns y."""
+    _mat(x, "x")
+    rows, cols = x.shape
+    _vec(w, cols, "w")
+    y = _out_like(y, x, "y")
+    st = _capi.lib().rmsnorm_f32_noalloc(x.data_ptr(), w.data_ptr(), y.data_ptr(), rows, cols, float(eps),
+                                          _plan_ptr(plan), _stream(stream))
+    _capi.check("rmsnorm_f32_noalloc", st)
     return y
 
 

@@ -55,7 +55,7 @@ EXPORTED = (
     "residual_layernorm_f32_ws", "cross_entropy_f32_ws",
     "rmsnorm_bf16_ws", "row_sum_bf16_ws", "softmax_bf16_ws", "layernorm_bf16_ws",
     "residual_layernorm_bf16_ws", "cross_entropy_bf16_ws",
-    "rr_workspace_bytes",
+    "rr_workspace_bytes", "rmsnorm_f32_noalloc",
     "rr_select_plan", "rr_check_plan", "rr_status_string",
     "rr_select_plan_from", "rr_model_time_us", "rr_batch",
     "rr_copy_f32", "rr_stream_f32", "rr_empty_kernel",
@@ -94,6 +94,7 @@ _planp = ctypes.POINTER(rr_plan)
 
 RR_BATCH_MAX = 32
 RR_MAX_COLS = (1 << 31) - (1 << 20)   # widest row (every kernel index fits in 32 bits)
+RR_NOALLOC_SCRATCH_BYTES = 1 << 20   # rmsnorm_f32_noalloc's static split-row buffer
 
 
 class rr_problem(ctypes.Structure):
@@ -152,6 +153,7 @@ _SIGNATURES = {
     "residual_layernorm_bf16_ws": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp, _i64, _vp],
     "cross_entropy_bf16_ws": [_vp, _vp, _vp, _i64, _i64, _planp, _vp, _i64, _vp],
     "rr_workspace_bytes": [ctypes.c_int, _i64, _i64, _planp],
+    "rmsnorm_f32_noalloc": [_vp, _vp, _vp, _i64, _i64, _f32, _planp, _vp],
     "rr_select_plan": [ctypes.c_int, _i64, _i64, _planp],
     "rr_check_plan": [ctypes.c_int, _i64, _i64, _planp],
     "rr_select_plan_from": [ctypes.c_int, _i64, _i64, ctypes.c_int, _planp],

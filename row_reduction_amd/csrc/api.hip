@@ -1,6 +1,7 @@
 // C entry points of librowred: argument validation, plan selection or check,
 // and the kernel launch(es) on the caller's stream. No allocation, no
-// synchronisation, no global mutable state.
+// synchronisation, and no state shared between calls other than the static
+// device buffer of rmsnorm_f32_noalloc (with its per-device address).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -243,6 +244,28 @@ extern "C" {
 int rmsnorm_f32_ws(const float *x, const float *w, float *y, int64_t rows, int64_t cols, float eps,
                    const rr_plan *plan, void *ws, int64_t wsb, void *stream) {
     return rmsnorm_call(RR_OP_RMSNORM, x, w, y, rows, cols, eps, plan, ws, wsb, stream);
+}
+int rmsnorm_f32_noalloc(const float *x, const float *w, float *y, int64_t rows, int64_t cols, float eps,
+                        const rr_plan *plan, void *stream) {
+    Operands o;
+    o.x = x;
+    o.w = w;
+    o.y = y;
+    o.rows = rows;
+    o.cols = cols;
+    o.eps = eps;
+    Args a;
+    int max_v;
+    int st = prepare(RR_OP_RMSNORM, o, &a, &max_v);
+    if (st != RR_OK || rows == 0) return st;
+    rr_plan p;
+    st = resolve_plan(RR_OP_RMSNORM, a, plan, RR_NOALLOC_SCRATCH_BYTES, max_v, &p);
+    if (st != RR_OK) return st;
+    if (p.path == RR_PATH_SPLIT) {
+        st = noalloc_scratch(&a.workspace);
+        if (st != RR_OK) return st;
+    }
+    return launch(RR_OP_RMSNORM, p, a, stream) == (int)hipSuccess ? RR_OK : RR_ERR_LAUNCH;
 }
 int rmsnorm_f32_ex(const float *x, const float *w, float *y, int64_t rows, int64_t cols, float eps,
                    const rr_plan *plan, void *stream) {
