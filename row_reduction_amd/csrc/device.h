@@ -465,16 +465,19 @@ __global__ void __launch_bounds__(1024) reg_kernel(const Args a) {
     }
 
     if constexpr (OP == kRmsNorm) {
-        // The weights are issued with the row so their latency hides behind
-        // the reduction; the epilogue then only multiplies and stores.
-        float wv[K];
-#pragma unroll
-        for (int c = 0; c < NCHUNK; ++c) load_slots<V, EXACT>(Wt, c * stride + base, cols, &wv[c * V], 0.0f);
         float t[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) t[k] = v[k] * v[k];
         const float ss = row_reduce(tree_reduce<K>(t, AddOp{}), AddOp{}, rl, lds0);
         const float inv = rsqrtf(ss / (float)cols + a.eps);
+        // The weights, which every row reads, are loaded after the reduction
+        // rather than with the row: issued at the start, every group asks
+        // for the same lines at once while the row loads are in flight
+        // (measured on MI355X: 16384x8192 1.4-2 % faster this way, bfloat16
+        // 1024x4096 8-15 %, bfloat16 16384x8192 1.4 % slower).
+        float wv[K];
+#pragma unroll
+        for (int c = 0; c < NCHUNK; ++c) load_slots<V, EXACT>(Wt, c * stride + base, cols, &wv[c * V], 0.0f);
         if (row_ok) {
 #pragma unroll
             for (int c = 0; c < NCHUNK; ++c) {
