@@ -745,6 +745,9 @@ def main() -> int:
     src_hash = device_source_hash()
     traffic = counter_traffic(kernel_hash)
 
+    # rr_copy_f32 over the same 2^30 bytes: the calibration kernel of the
+    # hardware byte counters (its reads and writes are known exactly).
+    calib = graph_us(torch, lambda: rr.rr_copy_f32(x.view(-1), y.view(-1)), 8, samples=5)
     ceilings = Ceilings(torch, rr, device)
     head_ceiling = ceilings.get(nbytes, False, True)
     empty = graph_us(torch, lambda: rr.rr_empty_kernel(), 200)
@@ -757,6 +760,8 @@ def main() -> int:
     head_parity = None
     if leg is not None:
         log("headline: full oracle check of the output")
+        step()  # y again (the calibration copy above overwrote it)
+        torch.cuda.synchronize()
         y_np = y.cpu().numpy()
         ref, secs, threads = leg.reference("rmsnorm", {"x": wl.x, "w": wl.w, "eps": wl.eps}, rows)
         head_parity = leg.check({"y": y_np}, ref, False)
@@ -790,6 +795,7 @@ def main() -> int:
         "headline": {"us_per_launch": avg_kernel_us, "GBps": achieved, "parity": head_parity,
                      "plan": plan_str(plan)},
         "stream_ceiling": head_ceiling, "launch_floor_us": round(empty["us"], 3),
+        "copy_2p30_bytes_us": round(calib["us"], 3),
         "device": device_info(torch), "cpu_baseline": cpu,
         "shapes": shapes, "long_rows": long_rows, "streaming_rows": streaming, "single_call": single,
     }

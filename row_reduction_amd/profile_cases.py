@@ -317,6 +317,92 @@ def counters(args) -> int:
     return 0
 
 
+def counters_cases(args) -> int:
+    """Per-case HBM traffic from two rocprofv3 --pmc runs of the same `run`
+    command (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), dispatches
+    attributed to the manifest's cases in order as in `summarize`. Each
+    counter is scaled by what it reads for the manifest's largest stream copy
+    (rr_stream_f32, --ceilings), whose reads and writes are each half of its
+    known bytes."""
+    man = json.load(open(args.manifest))
+
+    def per_entry(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if ours(r["Kernel_Name"]) and r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        out, pos = [], 0
+        for e in man["entries"]:
+            chunk = rows[pos:pos + e["count"]]
+            pos += e["count"]
+            if len(chunk) != e["count"]:
+                raise SystemExit(f"{counter}: trace ended early at {e['name']}")
+            out.append(sum(float(r["Counter_Value"]) for r in chunk) * 1024 / len(chunk))
+        if pos != len(rows):
+            raise SystemExit(f"{counter}: {len(rows) - pos} dispatches left unattributed")
+        return out
+
+    fetch = per_entry(args.fetch_csv, "FETCH_SIZE")
+    write = per_entry(args.write_csv, "WRITE_SIZE")
+    copies = [(i, e) for i, e in enumerate(man["entries"]) if e["kind"] == "stream" and "copy" in e["name"]
+              and not e["warmup"]]
+    if not copies:
+        raise SystemExit("the manifest holds no stream copy (run with --ceilings)")
+    ci, ce = max(copies, key=lambda ie: ie[1]["bytes"])
+    f_scale, w_scale = (ce["bytes"] / 2) / fetch[ci], (ce["bytes"] / 2) / write[ci]
+    print(f"Calibration: `{ce['name']}` must read and write {ce['bytes'] // 2} B each; "
+          f"FETCH_SIZE scale {f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f}.")
+    print()
+    print("| Case | Algorithmic B | FETCH_SIZE calibrated B | WRITE_SIZE calibrated B | traffic / algorithmic |")
+    print("|---|---:|---:|---:|---:|")
+    for i, e in enumerate(man["entries"]):
+        if e["warmup"] or not e["bytes"]:
+            continue
+        f, w = fetch[i] * f_scale, write[i] * w_scale
+        print(f"| {e['name']} | {e['bytes']} | {f:.0f} | {w:.0f} | {(f + w) / e['bytes']:.4f} |")
+    return 0
+
+
+def counters_table(args) -> int:
+    """Mean of every counter of one rocprofv3 --pmc run per manifest case
+    (dispatches attributed in order as in `summarize`), with what they give
+    per kernel. GRBM_GUI_ACTIVE is summed over the XCDs and, under counter
+    collection, carries a fixed overhead that the manifest's empty kernel
+    shows; the kernel's own active cycles per XCD are (GRBM_GUI_ACTIVE -
+    empty kernel's) / XCDs. From them: waves resident per CU on average
+    (SQ_WAVE_CYCLES / (active cycles x CUs)) and the fraction of the active
+    cycles the busiest texture-address unit (which every vector memory
+    access passes) was busy (TA_BUSY_max / active cycles)."""
+    man = json.load(open(args.manifest))
+    rows = [r for r in csv.DictReader(open(args.csv)) if ours(r["Kernel_Name"])]
+    names = sorted({r["Counter_Name"] for r in rows})
+    by_dispatch = {}
+    for r in rows:
+        by_dispatch.setdefault(int(r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    ids = sorted(by_dispatch)
+    pos = 0
+    means = []
+    for e in man["entries"]:
+        chunk = ids[pos:pos + e["count"]]
+        pos += e["count"]
+        if len(chunk) != e["count"]:
+            raise SystemExit(f"counters ended early at {e['name']}")
+        if not e["warmup"]:
+            means.append((e, {n: sum(by_dispatch[i].get(n, 0.0) for i in chunk) / len(chunk) for n in names}))
+    if pos != len(ids):
+        raise SystemExit(f"{len(ids) - pos} dispatches left unattributed")
+    base = next((m.get("GRBM_GUI_ACTIVE", 0.0) for e, m in means if e["kind"] == "empty"), 0.0)
+    print(f"Empty kernel's GRBM_GUI_ACTIVE (collection overhead, subtracted): {base:.0f}; XCDs {args.xcd}, CUs {args.cus}.")
+    print()
+    print("| Case | " + " | ".join(names) + " | active cycles per XCD | waves per CU | TA busy / active |")
+    print("|---|" + "---:|" * (len(names) + 3))
+    for e, m in means:
+        act = (m.get("GRBM_GUI_ACTIVE", 0.0) - base) / args.xcd
+        occ = m.get("SQ_WAVE_CYCLES", 0.0) / (act * args.cus) if act > 0 else float("nan")
+        ta = m.get("TA_BUSY_max", 0.0) / act if act > 0 else float("nan")
+        print(f"| {e['name']} | " + " | ".join(f"{m[n]:.0f}" for n in names) +
+              f" | {act:.0f} | {occ:.2f} | {ta:.3f} |")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -339,9 +425,22 @@ def main() -> int:
     c = sub.add_parser("counters")
     c.add_argument("fetch_csv")
     c.add_argument("write_csv")
+    cc = sub.add_parser("counters-cases")
+    cc.add_argument("manifest")
+    cc.add_argument("fetch_csv")
+    cc.add_argument("write_csv")
+    ct = sub.add_parser("counters-table")
+    ct.add_argument("manifest")
+    ct.add_argument("csv")
+    ct.add_argument("--cus", type=int, default=256)
+    ct.add_argument("--xcd", type=int, default=8)
     args = ap.parse_args()
+    if args.cmd == "counters-table":
+        return counters_table(args)
     if args.cmd == "counters":
         return counters(args)
+    if args.cmd == "counters-cases":
+        return counters_cases(args)
     if args.cmd == "run":
         if args.shapes:
             args.shapes = set(args.shapes.split(","))
