@@ -868,6 +868,97 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
         stream_second(emit, fill);
     };
 
+    // Second pass of the LayerNorms, whose outputs need gamma and beta. Each
+    // chunk's output needs AV weight values (load_aux), and
+    // the stores of a chunk keep the compiler from issuing later chunks'
+    // weight loads before them (they might alias), so a chunk-by-chunk pass
+    // waits one cache round trip per chunk. Here the weights of a batch of
+    // chunks are issued before any of that batch is stored: NBK chunks at a
+    // time among the register-kept ones, NBL among the LDS-kept ones, NBS
+    // among the streamed ones (whose row values are read in the same batch).
+    auto second_pass_w = [&](auto nbk, auto nbl, auto nbs, auto av, auto load_aux, auto emit, float fill) {
+        constexpr int NBK = decltype(nbk)::value, NBL = decltype(nbl)::value, NBS = decltype(nbs)::value;
+        constexpr int AV = decltype(av)::value;
+        // Kept chunks' offsets recomputed from an opaque copy of `base`
+        // rather than held in registers since the first pass.
+        int base2 = base;
+        asm volatile("" : "+v"(base2));
+#pragma unroll
+        for (int c0 = 0; c0 < KEEP; c0 += NBK) {
+            float aux[NBK][AV];
+#pragma unroll
+            for (int j = 0; j < NBK; ++j)
+                if (c0 + j < KEEP && c0 + j < nchunk) load_aux((c0 + j) * stride + base2, aux[j]);
+            // Keep the scheduler from moving the batch's arithmetic up between
+            // its loads (it would reuse their registers and wait on each).
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < NBK; ++j) {
+                if (c0 + j < KEEP && c0 + j < nchunk) {
+                    float d[V];
+#pragma unroll
+                    for (int e = 0; e < V; ++e) d[e] = keep[(c0 + j) * V + e];
+                    emit((c0 + j) * stride + base2, d, aux[j]);
+                }
+            }
+        }
+        auto lds_chunk = [&](int c, float *d) {
+            if constexpr (DMA) {
+                dma_read(c, d, fill);
+            } else {
+                lds_get(c, d);
+            }
+        };
+        int c = KEEP;
+        if constexpr (LDSC > 0) {
+            for (; c + NBL <= KEEP + ldsc; c += NBL) {
+                float aux[NBL][AV];
+#pragma unroll
+                for (int j = 0; j < NBL; ++j) load_aux((c + j) * stride + base, aux[j]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < NBL; ++j) {
+                    float d[V];
+                    lds_chunk(c + j, d);
+                    emit((c + j) * stride + base, d, aux[j]);
+                }
+            }
+            for (; c < KEEP + ldsc; ++c) {
+                float aux[AV], d[V];
+                load_aux(c * stride + base, aux);
+                lds_chunk(c, d);
+                emit(c * stride + base, d, aux);
+            }
+        }
+        for (; c + NBS <= nchunk; c += NBS) {
+            float d[NBS][V], aux[NBS][AV];
+#pragma unroll
+            for (int j = 0; j < NBS; ++j) read((c + j) * stride + base, d[j], fill);
+#pragma unroll
+            for (int j = 0; j < NBS; ++j) load_aux((c + j) * stride + base, aux[j]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < NBS; ++j) emit((c + j) * stride + base, d[j], aux[j]);
+        }
+        for (; c < nchunk; ++c) {
+            float d[V], aux[AV];
+            read(c * stride + base, d, fill);
+            load_aux(c * stride + base, aux);
+            emit(c * stride + base, d, aux);
+        }
+    };
+    // Batches of at most 32 weight values (4 chunks of gamma and beta at
+    // V = 4, 2 at V = 8), and streamed batches of at most 32 row and weight
+    // values together (LayerNorm 4096x65536: float 0.5-1 % faster than
+    // chunk by chunk, residual 1 %, bfloat16 1.5-2.2 %).
+    auto weighted_pass = [&](auto av, auto load_aux, auto emit, float fill) {
+        constexpr int AV = decltype(av)::value;
+        constexpr int NB = 32 / AV < 1 ? 1 : (32 / AV > 4 ? 4 : 32 / AV);
+        constexpr int NS = 32 / (V + AV) < 1 ? 1 : (32 / (V + AV) > 2 ? 2 : 32 / (V + AV));
+        second_pass_w(std::integral_constant<int, NB>{}, std::integral_constant<int, NB>{},
+                      std::integral_constant<int, NS>{}, av, load_aux, emit, fill);
+    };
+
     if constexpr (OP == kRmsNorm) {
         float acc = 0.0f;
         first_pass([&](int, const float *d) {
@@ -878,6 +969,8 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
         }, 0.0f);
         const float ss = row_reduce(acc, AddOp{}, rl, lds0);
         const float inv = rsqrtf(ss / (float)cols + a.eps);
+        // Chunk by chunk: batching the weight loads as the LayerNorms do
+        // measured 5 % slower here (4096x65536, float and bfloat16).
         second_pass([&](int i0, float *d) {
             float wv[V];
             load_window<V>(Wt, i0, cols, wv, 0.0f);
@@ -1063,13 +1156,17 @@ __device__ __forceinline__ void loop_row(const Args &a, const int64_t row) {
         const float rstd = (float)(1.0 / sqrt(var + (double)a.eps));
         const float mu = (float)rmean;  // row mean minus h0
         T *hr = (OP == kResidualLayerNorm && a.h_out != nullptr) ? static_cast<T *>(a.h_out) + off : nullptr;
-        second_pass([&](int i0, float *d) {
-            float g[V], b[V];
+        // aux holds gamma (first V values) then beta.
+        weighted_pass(std::integral_constant<int, 2 * V>{},
+                      [&](int i0, float *gb) {  // windows as is, as for RMSNorm's w
+                          const int st = window_start<V>(i0, cols);
+                          load_pack<V>(Wt + st, gb);
+                          load_pack<V>(B + st, gb + V);
+                      },
+                      [&](int i0, float *d, const float *gb) {
             if (hr != nullptr) store_guarded<V, HINT>(hr, i0, cols, cols, d);
-            load_window<V>(Wt, i0, cols, g, 0.0f);
-            load_window<V>(B, i0, cols, b, 0.0f);
 #pragma unroll
-            for (int e = 0; e < V; ++e) d[e] = ((d[e] - h0) - mu) * rstd * g[e] + b[e];
+            for (int e = 0; e < V; ++e) d[e] = ((d[e] - h0) - mu) * rstd * gb[e] + gb[V + e];
             store_guarded<V, HINT>(Y + off, i0, cols, cols, d);
         }, 0.0f);
     }

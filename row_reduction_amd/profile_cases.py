@@ -73,7 +73,9 @@ def cases_list(shapes_only=None, ops_only=None):
     # Streaming path: vocabulary-size rows and 65536-column normalisations.
     cases += [("cross_entropy", (2048, 128256)), ("cross_entropy_bf16", (2048, 128256)),
               ("softmax", (2048, 128256)), ("softmax_bf16", (2048, 128256)),
-              ("rmsnorm", (4096, 65536)), ("layernorm", (4096, 65536))]
+              ("rmsnorm", (4096, 65536)), ("layernorm", (4096, 65536)),
+              ("residual_layernorm", (4096, 65536)), ("rmsnorm_bf16", (4096, 65536)),
+              ("layernorm_bf16", (4096, 65536)), ("residual_layernorm_bf16", (4096, 65536))]
     if shapes_only:
         cases = [c for c in cases if f"{c[1][0]}x{c[1][1]}" in shapes_only]
     if ops_only:
