@@ -21,7 +21,7 @@ The LAST line on stdout is one compact JSON object (under 2 KB):
                 the oracle in this run, and how many failed
 
 Everything else goes to a detail file (--detail, default
-gpurun_out/bench_detail.json) and, one line per row, to stderr:
+bench_detail.json in the working directory) and, one line per row, to stderr:
 
   shapes          per (operator, shape, cache state): GPU us/op (median of
                   graph-replayed samples, raw samples kept), rows/s, GB/s and
@@ -691,7 +691,7 @@ def main() -> int:
                                                              "and single-call tables")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle (baseline and parity checks)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--detail", default=os.path.join("gpurun_out", "bench_detail.json"),
+    ap.add_argument("--detail", default="bench_detail.json",
                     help="where the full result (every table) is written")
     args = ap.parse_args()
 
