@@ -311,12 +311,14 @@ int cross_entropy_bf16_ws(const uint16_t *logits, const int32_t *targets, float 
  * buffer (rows * S * 16 bytes), else it picks as rmsnorm_f32 does; an
  * explicit split plan needing more returns RR_ERR_UNSUPPORTED before
  * anything is enqueued. Each GPU holds one such buffer, shared by every call
- * on that GPU, from the first call until the process ends; the address is
- * looked up once per device on the calling thread's current device, which
- * must be the device of `stream`. Nothing in it needs clearing (the first
- * launch of a split plan writes every partial the second one reads), but
- * calls that overlap on one GPU (other streams, other host threads) race on
- * it: serialise them, e.g. on one stream. Other arguments, ownership and
+ * on that GPU, from the first call until the process ends; the copy used is
+ * that of the device `stream` belongs to (for the null stream, the calling
+ * thread's current device), its address looked up once per device
+ * (RR_ERR_INVALID_ARGUMENT when the stream's device cannot be queried).
+ * Nothing in it needs clearing (the first launch of a split plan writes
+ * every partial the second one reads), but calls that overlap on one GPU
+ * (other streams, other host threads) race on it: serialise them, e.g. on
+ * one stream. Other arguments, ownership and
  * errors are as for rmsnorm_f32_ws (RR_ERR_LAUNCH also when the buffer's
  * device address cannot be obtained). */
 #define RR_NOALLOC_SCRATCH_BYTES ((int64_t)1 << 20)

@@ -262,7 +262,7 @@ int rmsnorm_f32_noalloc(const float *x, const float *w, float *y, int64_t rows, 
     st = resolve_plan(RR_OP_RMSNORM, a, plan, RR_NOALLOC_SCRATCH_BYTES, max_v, &p);
     if (st != RR_OK) return st;
     if (p.path == RR_PATH_SPLIT) {
-        st = noalloc_scratch(&a.workspace);
+        st = noalloc_scratch(stream, &a.workspace);
         if (st != RR_OK) return st;
     }
     return launch(RR_OP_RMSNORM, p, a, stream) == (int)hipSuccess ? RR_OK : RR_ERR_LAUNCH;

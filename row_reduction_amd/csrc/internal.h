@@ -43,11 +43,13 @@ int launch_layernorm_bf16(const rr_plan &p, const Args &a, void *stream);
 int launch_residual_layernorm_bf16(const rr_plan &p, const Args &a, void *stream);
 int launch_cross_entropy_bf16(const rr_plan &p, const Args &a, void *stream);
 
-// Device address, on the calling thread's current device, of the static
-// buffer rmsnorm_f32_noalloc keeps its split-row partials in
+// Device address, on the device `stream` belongs to (the calling thread's
+// current device for the null stream), of the static buffer
+// rmsnorm_f32_noalloc keeps its split-row partials in
 // (RR_NOALLOC_SCRATCH_BYTES); looked up once per device. RR_OK, or
-// RR_ERR_LAUNCH / RR_ERR_UNSUPPORTED when no address can be had.
-int noalloc_scratch(void **out);
+// RR_ERR_INVALID_ARGUMENT (the stream's device cannot be queried),
+// RR_ERR_UNSUPPORTED / RR_ERR_LAUNCH when no address can be had.
+int noalloc_scratch(void *stream, void **out);
 
 // Planner (plan.cpp; pure host C++).
 // max_v: widest pack the caller's pointer alignment allows (bfloat16 ops);

@@ -24,14 +24,27 @@ void *g_scratch_addr[kMaxDevices];  // written once per device, under its once_f
 
 }  // namespace
 
-int noalloc_scratch(void **out) {
+int noalloc_scratch(void *stream, void **out) {
+    // The kernels run on the stream's device, so the buffer is that
+    // device's copy (the null stream: the calling thread's current device).
     int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess) return RR_ERR_LAUNCH;
+    const hipError_t e = stream != nullptr ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
+                                           : hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return RR_ERR_INVALID_ARGUMENT;
+    }
     if (dev < 0 || dev >= kMaxDevices) return RR_ERR_UNSUPPORTED;
     std::call_once(g_scratch_once[dev], [dev] {
+        // The lookup answers for the current device: make it `dev` for the
+        // call and restore the caller's afterwards.
+        int prev = -1;
         void *addr = nullptr;
-        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_addr[dev] = addr;
-        else (void)hipGetLastError();  // a failed lookup must not fail the caller's later launches
+        if (hipGetDevice(&prev) == hipSuccess && (prev == dev || hipSetDevice(dev) == hipSuccess)) {
+            if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_addr[dev] = addr;
+            if (prev != dev) (void)hipSetDevice(prev);
+        }
+        (void)hipGetLastError();  // a failed lookup must not fail the caller's later launches
     });
     if (g_scratch_addr[dev] == nullptr) return RR_ERR_LAUNCH;
     *out = g_scratch_addr[dev];

@@ -12,7 +12,7 @@ before any scoring).
 from __future__ import annotations
 
 from . import _capi
-from ._capi import RR_OK, RR_PATH_LOOP, RR_PATH_PACKED, RR_PATH_ROW, rr_plan
+from ._capi import RR_OK, RR_PATH_LOOP, RR_PATH_PACKED, RR_PATH_ROW, RR_PATH_SPLIT, rr_plan
 
 PACKED_LANES = (8, 16, 32)
 PACKED_BLOCKS = (64, 256)
@@ -69,5 +69,5 @@ def candidate_plans(op: str, rows: int, cols: int, include_loop: bool = True,
 
 
 def plan_key(p: rr_plan) -> str:
-    name = {RR_PATH_PACKED: "packed", RR_PATH_ROW: "row", RR_PATH_LOOP: "loop"}[p.path]
+    name = {RR_PATH_PACKED: "packed", RR_PATH_ROW: "row", RR_PATH_LOOP: "loop", RR_PATH_SPLIT: "split"}[p.path]
     return f"{name}-b{p.block}-w{p.lanes_per_row}-v{p.v}-k{p.slots}-c{p.cache}"

@@ -253,6 +253,53 @@ def test_cross_entropy_out_of_range_targets_give_nan(gpu_device):
         assert_close(loss[[2, 3, 5]], oracle.cross_entropy(d["x"], t)[[2, 3, 5]], "ce valid rows")
 
 
+@pytest.mark.parametrize("bf16,cols", [(False, 257), (False, 4103), (False, 70001),
+                                       (True, 257), (True, 4104), (True, 70008)])
+def test_cross_entropy_out_of_range_targets_every_path(gpu_device, bf16, cols):
+    """A target outside [0, cols) gives loss NaN and leaves the other rows
+    within tolerance of the oracle on every path: each register and packed
+    plan, the streaming plans and the split plans, float and bfloat16 rows.
+    The kernels read the target logit from an in-row position whatever the
+    target, and replace it by NaN where the loss is formed."""
+    import torch
+    t = np.array([-1, cols, 0, cols - 1, 1 << 30, 5, -(1 << 31)], np.int32)
+    bad = np.array([True, True, False, False, True, False, True])
+    rows = len(t)
+    name = "cross_entropy_bf16" if bf16 else "cross_entropy"
+    if bf16:
+        x = workloads.family_inputs_bf16(rows, cols, seed=26 + cols)["x"]
+        ref = oracle.cross_entropy_bf16(x, t)
+        xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(gpu_device).view(torch.bfloat16)
+        call = rr.cross_entropy_bf16
+    else:
+        x = workloads.family_inputs(rows, cols, seed=26 + cols)["x"]
+        ref = oracle.cross_entropy(x, t)
+        xd = torch.from_numpy(x).to(gpu_device)
+        call = rr.cross_entropy_f32
+    assert np.isnan(ref[bad]).all() and np.isfinite(ref[~bad]).all()
+    td = torch.from_numpy(t).to(gpu_device)
+    cands = [(p, None) for p in [None] + plans.candidate_plans(name, rows, cols)]
+    for v in ((8, 4, 1) if bf16 else (4, 1)):
+        for block in (256, 1024):
+            lp = rr.rr_plan(2, block, block, 1, v, 0)
+            if rr.rr_check_plan(name, rows, cols, lp) == 0:
+                cands.append((lp, None))
+    for lanes, slots in ((64, 16), (256, 16), (1024, 32)):
+        sp = rr.rr_plan(3, lanes, lanes, 1, 8 if bf16 else 4, slots, 2)
+        if rr.rr_check_plan(name, rows, cols, sp) == 0:
+            cands.append((sp, torch.empty(rr.rr_workspace_bytes(name, rows, cols, sp), dtype=torch.uint8,
+                                          device=gpu_device)))
+    if cols > 65536:
+        assert any(ws is not None for _, ws in cands), "no split plan at this width"
+        assert any(p is not None and p.path == 2 for p, _ in cands), "no streaming plan at this width"
+    for p, ws in cands:
+        what = f"{name} {rows}x{cols} bad targets " + ("selected" if p is None else plans.plan_key(p))
+        announce(what)
+        loss = call(xd, td, plan=p, workspace=ws).cpu().numpy()
+        assert np.isnan(loss[bad]).all(), f"{what}: {loss[bad]}"
+        assert_close(loss[~bad], ref[~bad], what)
+
+
 @pytest.mark.parametrize("op", ["softmax", "cross_entropy"])
 @pytest.mark.parametrize("cols", [31, 129, 4103, 40000, 70001])
 def test_masked_entries_every_plan(gpu_device, op, cols):
