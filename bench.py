@@ -144,15 +144,22 @@ def host_cores() -> tuple[int, int]:
 
 
 def cpu_model() -> str:
-    cpu = platform.processor() or ""
+    """The host CPU's model name, with its family, model and stepping numbers
+    (which identify the generation where the name is generic, as it is on
+    some virtual machines: family 25 is Zen 3/4, 26 is Zen 5)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break  # the first processor's block is enough
+                k, _, v = line.partition(":")
+                fields[k.strip()] = v.strip()
     except OSError:
         pass
-    return cpu
+    name = fields.get("model name") or platform.processor() or "unknown"
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 # ---- same-bytes stream ceiling ----------------------------------------------------
