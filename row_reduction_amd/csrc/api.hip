@@ -59,9 +59,6 @@ int launch(int op, const rr_plan &p, const Args &a, void *stream) {
     }
 }
 
-// Everything after pointer validation: workspace check, plan (the caller's,
-// checked, or the selector's within max_v and the workspace), launch.
-// max_v bounds the pack width by the pointers' alignment (bfloat16 storage).
 // The plan a call runs: the caller's, checked (its pack width within max_v,
 // its workspace within `avail` bytes), or the selector's within both.
 int resolve_plan(int op, const Args &a, const rr_plan *plan, int64_t avail, int max_v, rr_plan *out) {
@@ -76,6 +73,9 @@ int resolve_plan(int op, const Args &a, const rr_plan *plan, int64_t avail, int 
     return select_plan(op, a.rows, a.cols, out, max_v, avail);
 }
 
+// Everything after pointer validation: workspace check, plan (the caller's,
+// checked, or the selector's within max_v and the workspace), launch.
+// max_v bounds the pack width by the pointers' alignment (bfloat16 storage).
 int run(int op, Args a, const rr_plan *plan, void *workspace, int64_t workspace_bytes, int max_v,
         void *stream) {
     if (workspace_bytes < 0 || !ok_opt(workspace, 16)) return RR_ERR_INVALID_ARGUMENT;
