@@ -3,6 +3,9 @@ plan the library selects (table, else the analytic model), with and without
 a split-row workspace, each compared element by element with the CPU
 oracle. The fixed parity matrix names its plans; this covers whatever the
 selector picks across the shape space."""
+import os
+import time
+
 import numpy as np
 import pytest
 
@@ -141,3 +144,82 @@ def test_masked_rows_on_random_shapes(gpu_device, op):
             ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu_device)
             announce(what + " with workspace")
             compare(op, run_f32(op, d, None, ws, gpu_device), ref, what + " ws")
+
+
+def test_long_campaign(gpu_device):
+    """Opt-in, time-bounded campaign (ROWRED_FUZZ_SECONDS; ROWRED_FUZZ_SEED
+    picks the seeds): round after round of random shapes for every operator,
+    each checked against the oracle with the selected plan (with and without
+    a workspace), three random legal plans of the candidate grid, random
+    explicit split plans and, for RMSNorm, the allocation-free entry point;
+    bfloat16 storage with the selected and three random plans. Every
+    mismatch is collected and reported together."""
+    import torch
+    budget = float(os.environ.get("ROWRED_FUZZ_SECONDS", "0"))
+    if budget <= 0:
+        pytest.skip("set ROWRED_FUZZ_SECONDS to run the long campaign")
+    base = int(os.environ.get("ROWRED_FUZZ_SEED", "50000"))
+    t0 = time.time()
+    fails, n = [], 0
+
+    def check(what, fn):
+        nonlocal n
+        n += 1
+        try:
+            fn()
+        except AssertionError as e:
+            fails.append(f"{what}: {str(e)[:300]}")
+
+    rnd = 0
+    while time.time() - t0 < budget:
+        for k, op in enumerate(OPS):
+            eps = workloads.RMSNORM_EPS if op == "rmsnorm" else workloads.LAYERNORM_EPS
+            rng = np.random.default_rng(base + 97 * rnd + k)
+            for i, (rows, cols) in enumerate(shapes(base + 1000 * rnd + 10 * k, 4, max_elems=1 << 21)):
+                seed = base + 100000 * rnd + 1000 * k + i
+                a = family_host_inputs(op, rows, cols, seed=seed)
+                ref = run_oracle(op, a)
+                d = to_dev(a, gpu_device)
+                check(f"selected {op} {rows}x{cols}",
+                      lambda: compare(op, run_f32(op, d, None, None, gpu_device), ref, "selected"))
+                nb = rr.rr_workspace_bytes(op, rows, cols)
+                if nb > 0:
+                    ws = torch.empty(nb, dtype=torch.uint8, device=gpu_device)
+                    check(f"workspace {op} {rows}x{cols}",
+                          lambda: compare(op, run_f32(op, d, None, ws, gpu_device), ref, "workspace"))
+                cands = plans.candidate_plans(op, rows, cols, caches=(0, 1, 2))
+                for j in rng.choice(len(cands), size=min(3, len(cands)), replace=False):
+                    p = cands[int(j)]
+                    check(f"plan {op} {rows}x{cols} {plans.plan_key(p)}",
+                          lambda: compare(op, run_f32(op, d, p, None, gpu_device), ref, "plan"))
+                for lanes, slots in ((64, 16), (128, 32), (256, 16), (512, 32), (1024, 16), (1024, 32)):
+                    sp = rr.rr_plan(3, lanes, lanes, 1, 4, slots, 2)
+                    if rr.rr_check_plan(op, rows, cols, sp) == 0 and rng.random() < 0.5:
+                        ws = torch.empty(rr.rr_workspace_bytes(op, rows, cols, sp), dtype=torch.uint8,
+                                         device=gpu_device)
+                        check(f"split {op} {rows}x{cols} {plans.plan_key(sp)}",
+                              lambda: compare(op, run_f32(op, d, sp, ws, gpu_device), ref, "split"))
+                if op == "rmsnorm":
+                    y = torch.empty_like(d["x"])
+
+                    def no_alloc():
+                        got = rr.rmsnorm_f32_noalloc(d["x"], d["w"], float(a["eps"]), y)
+                        torch.cuda.synchronize()
+                        compare(op, {"y": got}, ref, "no-alloc")
+                    check(f"no-alloc {rows}x{cols}", no_alloc)
+                c8 = max(8, cols - cols % 8) if i % 2 else cols
+                db = workloads.family_inputs_bf16(rows, c8, seed=seed + 7)
+                refb = run_oracle_bf16(op, db, eps)
+                t = dev_inputs_bf16(db, gpu_device)
+                name = op + "_bf16"
+                check(f"selected {name} {rows}x{c8}",
+                      lambda: compare_bf16(rename(run_bf16(op, t, None, None)), refb, "selected"))
+                cands = plans.candidate_plans(name, rows, c8, caches=(0, 1, 2))
+                for j in rng.choice(len(cands), size=min(3, len(cands)), replace=False):
+                    p = cands[int(j)]
+                    check(f"plan {name} {rows}x{c8} {plans.plan_key(p)}",
+                          lambda: compare_bf16(rename(run_bf16(op, t, p, None)), refb, "plan"))
+            announce(f"long campaign: round {rnd} {op}, {n} checks, {len(fails)} mismatches, "
+                     f"{time.time() - t0:.0f} s")
+        rnd += 1
+    assert not fails, f"{len(fails)} of {n} checks failed:\n" + "\n".join(fails[:20])
