@@ -17,7 +17,7 @@ from test_gpu_batch import rename
 from test_gpu_bf16 import compare as compare_bf16
 from test_gpu_bf16 import dev_inputs as dev_inputs_bf16
 from test_gpu_bf16 import run_oracle as run_oracle_bf16
-from test_gpu_split import run_bf16, run_f32
+from test_gpu_split import IN_PLACE_OPS, run_bf16, run_f32, run_in_place
 
 pytestmark = pytest.mark.gpu
 
@@ -151,9 +151,11 @@ def test_long_campaign(gpu_device):
     picks the seeds): round after round of random shapes for every operator,
     each checked against the oracle with the selected plan (with and without
     a workspace), three random legal plans of the candidate grid, random
-    explicit split plans and, for RMSNorm, the allocation-free entry point;
-    bfloat16 storage with the selected and three random plans. Every
-    mismatch is collected and reported together."""
+    explicit split plans, for the per-element operators one random plan
+    with y aliasing x (split plans included) and, for RMSNorm, the
+    allocation-free entry point; bfloat16 storage with the selected and
+    three random plans. Every mismatch is collected and reported
+    together."""
     import torch
     budget = float(os.environ.get("ROWRED_FUZZ_SECONDS", "0"))
     if budget <= 0:
@@ -199,6 +201,17 @@ def test_long_campaign(gpu_device):
                                          device=gpu_device)
                         check(f"split {op} {rows}x{cols} {plans.plan_key(sp)}",
                               lambda: compare(op, run_f32(op, d, sp, ws, gpu_device), ref, "split"))
+                if op in IN_PLACE_OPS:
+                    splits = [rr.rr_plan(3, w, w, 1, 4, k, 2) for w in (64, 256, 1024) for k in (16, 32)]
+                    pool = cands + [sp for sp in splits if rr.rr_check_plan(op, rows, cols, sp) == 0]
+                    p = pool[int(rng.integers(0, len(pool)))]
+                    ws = None
+                    if p.path == 3:
+                        ws = torch.empty(rr.rr_workspace_bytes(op, rows, cols, p), dtype=torch.uint8,
+                                         device=gpu_device)
+                    fresh = to_dev(a, gpu_device)
+                    check(f"in-place {op} {rows}x{cols} {plans.plan_key(p)}",
+                          lambda: compare(op, run_in_place(op, fresh, p, ws, False), ref, "in-place"))
                 if op == "rmsnorm":
                     y = torch.empty_like(d["x"])
 
