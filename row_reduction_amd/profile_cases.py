@@ -265,17 +265,30 @@ def summarize(args) -> int:
         med = statistics.median(durs)
         avg = sum(durs) / len(durs)
         gbps = e["bytes"] / med if e["bytes"] else None
-        out.append((e, chunk[0]["Kernel_Name"], len(durs), avg, med, durs[0], durs[-1], gbps))
+        # The span from the first start to the last end over the launch
+        # count: how far apart the profiled launches ran (under the profiler
+        # a graph's launches are spaced by its per-dispatch work).
+        span = (max(int(r["End_Timestamp"]) for r in chunk) - min(int(r["Start_Timestamp"]) for r in chunk)) / len(chunk)
+        out.append((e, chunk[0]["Kernel_Name"], len(durs), avg, med, durs[0], durs[-1], gbps, span))
     if pos != len(rows):
         raise SystemExit(f"{len(rows) - pos} librowred dispatches left unattributed")
-    print("| Case | Kernel | Launches | Avg ns | Median ns | Min ns | Max ns | GB/s (median) | % of 8 TB/s |")
-    print("|---|---|---:|---:|---:|---:|---:|---:|---:|")
-    for e, kname, n, avg, med, lo, hi, gbps in out:
+    spans = not man.get("isolated", False)
+    head = "| Case | Kernel | Launches | Avg ns | Median ns | Min ns | Max ns | GB/s (median) | % of 8 TB/s |"
+    rule = "|---|---|---:|---:|---:|---:|---:|---:|---:|"
+    if spans:
+        head += " Span per launch ns |"
+        rule += "---:|"
+    print(head)
+    print(rule)
+    for e, kname, n, avg, med, lo, hi, gbps, span in out:
         k = demangle(kname).replace("rowred::", "").replace("(rowred::Args)", "").replace("void ", "")
         k = k.replace("(anonymous namespace)::", "")
         g = f"{gbps:.1f}" if gbps else "—"
         f = f"{100 * gbps / PEAK_GBPS:.1f}" if gbps else "—"
-        print(f"| {e['name']} | `{k}` | {n} | {avg:.0f} | {med:.0f} | {lo} | {hi} | {g} | {f} |")
+        line = f"| {e['name']} | `{k}` | {n} | {avg:.0f} | {med:.0f} | {lo} | {hi} | {g} | {f} |"
+        if spans:
+            line += f" {span:.0f} |"
+        print(line)
     return 0
 
 
