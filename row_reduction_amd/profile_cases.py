@@ -1,7 +1,7 @@
 """Kernel-duration profile of every measured (operator, shape) under rocprofv3.
 
 `run` launches each case with the plan the library selects — warm-up launches
-first, then `--launches` measured ones back to back from one HIP graph, cache-hot (one buffer set) and, for
+first, then `--launches` measured ones from one HIP graph, cache-hot (one buffer set) and, for
 working sets of 1 MiB or more, cache-cold (cycling >= 768 MiB of distinct
 buffers) — plus the library's same-bytes streaming copy and empty kernel, and
 writes a manifest of what it launched, in order. Run it under
@@ -20,9 +20,20 @@ cross-entropy), rotated over buffers the same way.
 dispatch order, attributes them to the manifest's cases (checking each
 dispatch's grid size against the case's), and prints a markdown table of
 kernel durations with algorithmic GB/s and the fraction of the 8 TB/s HBM
-peak:
+peak, and for graph runs the span per launch (first start to last end over
+the launch count; under the profiler a graph's launches run spaced apart,
+so short kernels start on an idle GPU):
 
   python3 <repo>/row_reduction_amd/profile_cases.py summarize OUT/manifest.json OUT/cases_kernel_trace.csv
+
+Counter summaries, from `rocprofv3 --pmc` runs (one counter block per run):
+`counters` gives the headline kernel's HBM traffic from FETCH_SIZE and
+WRITE_SIZE runs of bench.py, calibrated by rr_copy_f32 of known bytes;
+`counters-cases` the same per case of a `run --ceilings` manifest,
+calibrated by that run's largest stream copy; `counters-table` lays out any
+counters of such a run per case, with GRBM_GUI_ACTIVE net of the empty
+kernel's, per XCD, and derived waves per CU and texture-address busy
+fraction.
 """
 from __future__ import annotations
 
