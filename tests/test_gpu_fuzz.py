@@ -153,9 +153,9 @@ def test_long_campaign(gpu_device):
     a workspace), three random legal plans of the candidate grid, random
     explicit split plans, for the per-element operators one random plan
     with y aliasing x (split plans included) and, for RMSNorm, the
-    allocation-free entry point; bfloat16 storage with the selected and
-    three random plans. Every mismatch is collected and reported
-    together."""
+    allocation-free entry point; bfloat16 storage with the selected plan,
+    three random plans and one in place. Every mismatch is collected and
+    reported together."""
     import torch
     budget = float(os.environ.get("ROWRED_FUZZ_SECONDS", "0"))
     if budget <= 0:
@@ -232,6 +232,18 @@ def test_long_campaign(gpu_device):
                     p = cands[int(j)]
                     check(f"plan {name} {rows}x{c8} {plans.plan_key(p)}",
                           lambda: compare_bf16(rename(run_bf16(op, t, p, None)), refb, "plan"))
+                if op in IN_PLACE_OPS:
+                    splits = [rr.rr_plan(3, w, w, 1, 8, k, 2) for w in (64, 256, 1024) for k in (16, 32)]
+                    pool = cands + [sp for sp in splits if rr.rr_check_plan(name, rows, c8, sp) == 0]
+                    p = pool[int(rng.integers(0, len(pool)))]
+                    ws = None
+                    if p.path == 3:
+                        ws = torch.empty(rr.rr_workspace_bytes(name, rows, c8, p), dtype=torch.uint8,
+                                         device=gpu_device)
+                    fresh = dict(dev_inputs_bf16(db, gpu_device), eps=eps)
+                    fresh["w"] = fresh["gamma"]
+                    check(f"in-place {name} {rows}x{c8} {plans.plan_key(p)}",
+                          lambda: compare_bf16(rename(run_in_place(op, fresh, p, ws, True)), refb, "in-place"))
             announce(f"long campaign: round {rnd} {op}, {n} checks, {len(fails)} mismatches, "
                      f"{time.time() - t0:.0f} s")
         rnd += 1
