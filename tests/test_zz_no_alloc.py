@@ -96,3 +96,39 @@ def test_noalloc_binding_plain_shape(gpu_device):
     y = rr.rmsnorm_f32_noalloc(x, w, wl.eps)
     torch.cuda.synchronize()
     assert_close(y.cpu().numpy(), oracle.rmsnorm(wl.x, wl.w, wl.eps), "noalloc 64x4096")
+
+
+@pytest.mark.gpu
+def test_noalloc_on_a_non_default_stream(gpu_device):
+    """On a stream of its own (a non-null handle, so the buffer is found
+    through the stream's device rather than the current one) the results
+    equal rmsnorm_f32_ws's on that stream bit for bit."""
+    import torch
+    rows, cols = 4, 1 << 20
+    wl = workloads.rmsnorm_workload(rows, cols, seed=4200)
+    x = torch.from_numpy(wl.x).to(gpu_device)
+    w = torch.from_numpy(wl.w).to(gpu_device)
+    sel_ws = rr.rr_workspace_bytes("rmsnorm", rows, cols)
+    assert 0 < sel_ws <= _capi.RR_NOALLOC_SCRATCH_BYTES
+    ws = torch.empty(sel_ws, dtype=torch.uint8, device=gpu_device)
+    y_ws = torch.full_like(x, float("nan"))
+    y_na = torch.full_like(x, float("nan"))
+    torch.cuda.synchronize()
+    L = _capi.lib()
+    s = torch.cuda.Stream(device=gpu_device)
+    announce("rmsnorm_f32_noalloc 4x1048576 on its own stream")
+    with torch.cuda.stream(s):
+        handle = _stream()
+        assert handle.value, "expected a non-null stream handle"
+        st = L.rmsnorm_f32_ws(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+                              ctypes.c_void_p(y_ws.data_ptr()), rows, cols, wl.eps, None,
+                              ctypes.c_void_p(ws.data_ptr()), sel_ws, handle)
+        assert st == _capi.RR_OK, _capi.status_string(st)
+        st = L.rmsnorm_f32_noalloc(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+                                   ctypes.c_void_p(y_na.data_ptr()), rows, cols, wl.eps, None, handle)
+        assert st == _capi.RR_OK, _capi.status_string(st)
+    s.synchronize()
+    got_ws = y_ws.cpu().numpy()
+    got_na = y_na.cpu().numpy()
+    assert np.array_equal(got_na.view(np.int32), got_ws.view(np.int32)), "differs from rmsnorm_f32_ws"
+    assert_close(got_na, oracle.rmsnorm(wl.x, wl.w, wl.eps), "noalloc on its own stream")
