@@ -132,3 +132,40 @@ def test_noalloc_on_a_non_default_stream(gpu_device):
     got_na = y_na.cpu().numpy()
     assert np.array_equal(got_na.view(np.int32), got_ws.view(np.int32)), "differs from rmsnorm_f32_ws"
     assert_close(got_na, oracle.rmsnorm(wl.x, wl.w, wl.eps), "noalloc on its own stream")
+
+
+@pytest.mark.gpu
+def test_noalloc_under_graph_capture(gpu_device):
+    """Captured into a HIP graph, as callers that cannot allocate use it (the
+    capture stream is not the null stream; an eager call first looks the
+    buffer up outside the capture): every replay, with new inputs copied in
+    and eager work and synchronisations between replays, equals the eager
+    rmsnorm_f32_ws call on the same inputs bit for bit."""
+    import torch
+    rows, cols = 4, 1 << 20
+    loads = [workloads.rmsnorm_workload(rows, cols, seed=4300 + i) for i in range(3)]
+    eps = loads[0].eps
+    assert all(wl.eps == eps for wl in loads)
+    x = torch.from_numpy(loads[0].x).to(gpu_device)
+    w = torch.from_numpy(loads[0].w).to(gpu_device)
+    y = torch.empty_like(x)
+    announce("rmsnorm_f32_noalloc 4x1048576 under graph capture")
+    rr.rmsnorm_f32_noalloc(x, w, eps, y)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rr.rmsnorm_f32_noalloc(x, w, eps, y)
+    torch.cuda.synchronize()
+    ws = torch.empty(rr.rr_workspace_bytes("rmsnorm", rows, cols), dtype=torch.uint8, device=gpu_device)
+    for i, wl in enumerate(loads):
+        x.copy_(torch.from_numpy(wl.x))
+        w.copy_(torch.from_numpy(wl.w))
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        replayed = y.clone()
+        ref = rr.rmsnorm_f32(x, w, eps, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(replayed.view(torch.int32), ref.view(torch.int32)), f"replay {i}"
+        assert_close(replayed.cpu().numpy(), oracle.rmsnorm(wl.x, wl.w, wl.eps), f"graph replay {i}")
